@@ -1,0 +1,174 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 W4A4 linear-layer library.
+ *
+ * The format, as the pages on arXiv 2609.04098 ("Why Gated DeltaNet Survives
+ * 4-Bit Quantization: NVFP4 W4A4 for the Recurrent Half of a Hybrid 27B LLM")
+ * define it: picx.dev summary, "Introduction and Theoretical Foundation" >
+ * "Background", item 1 -- each value is a 4-bit E2M1 float, each block of 16
+ * consecutive values has one E4M3 scale set to the block's absolute maximum
+ * divided by 6, and the tensor has one FP32 scale; anthology record LIT-800,
+ * "Standing in the anthology" -- 16-element blocks with an E4M3 scale, where
+ * MX uses 32 elements and a power-of-two scale.
+ *
+ * Exact semantics implemented (the pages leave the arithmetic open; this is
+ * the plainest reading, applied bit-exactly):
+ *   g      = RN32(amax / 2688), or 1.0 if that is 0          (tensor scale)
+ *   s_blk  = E4M3 round-to-nearest-even of blockmax / (6 g), exact real
+ *            quotient, saturated at 448 (0x7E); subnormals kept; 0 allowed
+ *   code   = sign(x) << 3 | E2M1 round-to-nearest-even of |x| / (s_blk g),
+ *            exact real quotient, saturated at 6; zero scale -> magnitude 0
+ *   deq(x) = E2M1(code) * E4M3(s_blk) * g
+ * Codes are packed two per byte (even column in the low nibble) into a
+ * row-major [rows x cols/2] array; scales are a row-major [rows x cols/16]
+ * array of E4M3 ("fn" variant: bias 7, no infinity, 0x7F = NaN) bytes.
+ * Blocks run along the contraction dimension K of both GEMM operands, so
+ * weights are stored [N x K] (out x in), K contiguous.
+ *
+ * Conventions shared by every call:
+ *   - Every tensor pointer is a DEVICE pointer (hipMalloc'd or from torch);
+ *     host pointers are named as such.  The caller owns every buffer; the
+ *     library allocates nothing and keeps no mutable global state.
+ *   - Calls enqueue work on `stream` (a hipStream_t, passed as void*; NULL is
+ *     the default stream) and return without synchronizing.  Tensor scales
+ *     stay on the device: no host<->device copy happens inside a call.
+ *   - All argument checks run before any HIP call.  A failed check returns
+ *     its status and enqueues nothing.  A failed kernel launch returns
+ *     NVFP4_ERR_HIP (see nvfp4_last_hip_error).  Faults inside a kernel
+ *     surface asynchronously through HIP, as for any kernel.
+ *   - Rows == 0 is a valid no-op.  Exceptions never cross the ABI.  Calls on
+ *     different streams are independent; calls that write the same buffers
+ *     concurrently race.
+ *   - Bit-exactness against the exact-real definition above holds for tensor
+ *     scales g in [2^-100, 2^100] (amax in [2^-88, 2^111] for computed
+ *     scales) and finite inputs.  Non-finite inputs give unspecified codes.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef NVFP4_API
+#define NVFP4_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,      /* a required pointer is NULL                       */
+  NVFP4_ERR_SHAPE = 2,     /* bad size: negative, K/cols % 16 != 0, ld < cols */
+  NVFP4_ERR_DTYPE = 3,     /* unknown input/output dtype code                  */
+  NVFP4_ERR_MODE = 4,      /* unknown scale mode                               */
+  NVFP4_ERR_ALIGN = 5,     /* a pointer is not aligned as documented           */
+  NVFP4_ERR_WORKSPACE = 6, /* workspace too small                              */
+  NVFP4_ERR_HIP = 7,       /* a HIP launch failed; see nvfp4_last_hip_error()  */
+  NVFP4_ERR_ALIAS = 8      /* an output overlaps an input it must not overlap  */
+} nvfp4_status_t;
+
+typedef enum { NVFP4_IN_F32 = 0, NVFP4_IN_BF16 = 1 } nvfp4_in_t;
+typedef enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 } nvfp4_out_t;
+typedef enum { NVFP4_SCALE_GIVEN = 0, NVFP4_SCALE_FROM_AMAX = 1 } nvfp4_scale_mode_t;
+
+/*
+ * nvfp4_quantize -- NVFP4 encode of a row-major [rows x cols] tensor
+ * (picx.dev summary, "Background", item 1: E2M1 values, one E4M3 scale of
+ * blockmax/6 per 16 values, one FP32 tensor scale).
+ *
+ *   x            device, [rows x ldx] elements of type `in_dtype`
+ *                (NVFP4_IN_F32 or NVFP4_IN_BF16); 16-byte aligned, and
+ *                ldx * element size a multiple of 16 bytes
+ *   rows, cols   rows >= 0; cols > 0 and cols % 16 == 0
+ *   ldx          row stride of x in elements, ldx >= cols
+ *   codes        device out, [rows x cols/2] bytes, 8-byte aligned
+ *   scales       device out, [rows x cols/16] E4M3 bytes
+ *   global_scale device, one float.  NVFP4_SCALE_GIVEN: read (the caller's
+ *                positive finite calibrated scale g).  NVFP4_SCALE_FROM_AMAX:
+ *                written with g = RN32(amax/2688) (1.0 if that is 0) computed
+ *                from x, then used.
+ *   mode         nvfp4_scale_mode_t
+ *   stream       hipStream_t or NULL
+ * FROM_AMAX enqueues four kernels (clear, absolute-max reduction, encode,
+ * finalize); GIVEN enqueues one.  Output is deterministic.
+ */
+NVFP4_API nvfp4_status_t nvfp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t cols,
+                              int64_t ldx, uint8_t* codes, uint8_t* scales,
+                              float* global_scale, int32_t mode, void* stream);
+
+/*
+ * nvfp4_gemm -- W4A4 linear layer y = (g_a g_w) * deq(A) * deq(W)^T
+ * (picx.dev summary, "Background", item 1: both operands NVFP4, multiplied
+ * as 4-bit values; the MI355X path dequantizes each E2M1 x E4M3 product
+ * exactly to fp16 and accumulates in fp32 on the matrix cores, then applies
+ * RN32(g_a g_w) in the epilogue).
+ *
+ *   a_codes, a_scales  device, A = [M x K] activations in the layout above
+ *   a_gs               device, one float: g_a
+ *   w_codes, w_scales  device, W = [N x K] weights in the layout above
+ *   w_gs               device, one float: g_w
+ *   M, N, K            M >= 0, N > 0, K > 0, K % 16 == 0
+ *   y                  device out, [M x ldy] of `out_dtype` (NVFP4_OUT_F32 or
+ *                      NVFP4_OUT_BF16, round-to-nearest-even); ldy >= N
+ *   workspace          device scratch or NULL; nvfp4_gemm_workspace_size()
+ *                      bytes are required (0 for every shape today)
+ * Fast path: K % 128 == 0 and codes/scales base pointers 16-/8-byte aligned;
+ * other K % 16 == 0 shapes take a slower generic kernel with the same result.
+ * Accuracy: |y - Y| <= 1e-4 * sum_k |a_k w_k| against the exact product for
+ * fp32 output (plus half a bf16 ulp of Y for bf16 output).  Deterministic:
+ * the same inputs give bit-identical output.
+ */
+NVFP4_API nvfp4_status_t nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                          const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
+                          int64_t M, int64_t N, int64_t K, void* y, int32_t out_dtype,
+                          int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_harmonize_fused_scales -- re-express the block scales of modules
+ * that are concatenated along N into one fused weight, each quantized with
+ * its own tensor scale g_i, under one shared tensor scale g* = max_i g_i
+ * (cctest.ai article "Why Gated DeltaNet Holds Up Under 4-Bit
+ * Quantization", "Main findings", last bullet: fusing independently
+ * calibrated GDN projections into one GEMM creates a global-scale mismatch,
+ * and the released checkpoint is pre-harmonized; LIT-800 "Standing in the
+ * anthology": the fused kernels computed the decay and write gates with
+ * mis-scaled weights).  The procedure itself is not on the pages; this call
+ * implements: every block scale s of module i becomes
+ * E4M3_RNE(E4M3(s) * g_i / g*) (exact real quotient, saturated); codes are
+ * left unchanged.  Afterwards a single nvfp4_gemm with w_gs = shared_gs
+ * serves the fused weight.
+ *
+ *   scales       device, in/out, [sum(module_rows) x K/16] E4M3 bytes,
+ *                modules concatenated along N in order
+ *   module_gs    device, n_modules floats g_i (positive, finite)
+ *   module_rows  HOST, n_modules row counts (each >= 0)
+ *   n_modules    1 .. 64
+ *   K            K > 0, K % 16 == 0
+ *   shared_gs    device out, one float: g*; must not overlap module_gs
+ *                (NVFP4_ERR_ALIAS)
+ *   counters     device out or NULL, two uint32: [0] blocks whose rescale is
+ *                inexact (E4M3(s') g* != E4M3(s) g_i), [1] nonzero input
+ *                scales whose result has a zero exponent field (subnormal
+ *                or zero)
+ * Enqueues two kernels (clear counters + rescale).
+ */
+NVFP4_API nvfp4_status_t nvfp4_harmonize_fused_scales(uint8_t* scales, const float* module_gs,
+                                            const int64_t* module_rows, int32_t n_modules,
+                                            int64_t K, float* shared_gs, uint32_t* counters,
+                                            void* stream);
+
+/* Bytes of workspace nvfp4_gemm needs for this shape (0 today). */
+NVFP4_API size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t out_dtype);
+
+/* Static description of a status code; never NULL. */
+NVFP4_API const char* nvfp4_status_string(int32_t status);
+
+/* hipError_t of the most recent failed launch on the calling thread (0 if none). */
+NVFP4_API int32_t nvfp4_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

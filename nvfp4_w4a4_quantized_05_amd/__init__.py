@@ -1,0 +1,14 @@
+"""MI355X-native NVFP4 W4A4 linear layer: quantize, GEMM, fused-scale harmonize.
+
+The computation lives in ``libnvfp4.so`` (hand-written HIP for gfx950 behind
+the C ABI of ``include/nvfp4.h``); this package is its thin Python binding.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    Nvfp4Error,
+    gemm,
+    harmonize_fused_scales,
+    load,
+    quantize,
+)

@@ -1,0 +1,161 @@
+"""ctypes binding of ``libnvfp4.so``: argument marshalling only.
+
+Names mirror the C ABI in ``include/nvfp4.h``.  torch supplies device memory
+and the current stream; every step of the computation runs in the HIP
+library.  There is no fallback: if the library is missing, or a tensor is not
+on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
+
+NVFP4_OK = 0
+IN_F32, IN_BF16 = 0, 1
+OUT_F32, OUT_BF16 = 0, 1
+SCALE_GIVEN, SCALE_FROM_AMAX = 0, 1
+STATUS_NAMES = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_DTYPE",
+                4: "NVFP4_ERR_MODE", 5: "NVFP4_ERR_ALIGN", 6: "NVFP4_ERR_WORKSPACE",
+                7: "NVFP4_ERR_HIP", 8: "NVFP4_ERR_ALIAS"}
+EXPORTS = ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_harmonize_fused_scales",
+           "nvfp4_gemm_workspace_size", "nvfp4_status_string", "nvfp4_last_hip_error")
+
+_lib = None
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = load().nvfp4_status_string(status).decode()
+        if status == 7:
+            msg += f" (hipError {load().nvfp4_last_hip_error()})"
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)}: {msg}")
+
+
+def load() -> ctypes.CDLL:
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m nvfp4_w4a4_quantized_05_amd.build` (needs hipcc)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.nvfp4_quantize.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i32, vp]
+    lib.nvfp4_quantize.restype = i32
+    lib.nvfp4_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp, sz, vp]
+    lib.nvfp4_gemm.restype = i32
+    lib.nvfp4_harmonize_fused_scales.argtypes = [vp, vp, ctypes.POINTER(i64), i32, i64, vp, vp, vp]
+    lib.nvfp4_harmonize_fused_scales.restype = i32
+    lib.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64, i32]
+    lib.nvfp4_gemm_workspace_size.restype = sz
+    lib.nvfp4_status_string.argtypes = [i32]
+    lib.nvfp4_status_string.restype = ctypes.c_char_p
+    lib.nvfp4_last_hip_error.argtypes = []
+    lib.nvfp4_last_hip_error.restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != NVFP4_OK:
+        raise Nvfp4Error(status, what)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("nvfp4 calls take GPU tensors only")
+
+
+def quantize(x: torch.Tensor, global_scale: torch.Tensor | None = None, *, from_amax: bool | None = None,
+             codes: torch.Tensor | None = None, scales: torch.Tensor | None = None, stream=None):
+    """NVFP4-encode a 2-D bf16 or fp32 GPU tensor (rows contiguous, any row stride).
+
+    ``global_scale`` is a one-element fp32 GPU tensor: read when it is given
+    (calibrated scale), written with RN32(amax/2688) when ``from_amax``
+    (default: from_amax = global_scale is None).  Returns (codes, scales, gs).
+    """
+    _need_gpu(x, global_scale, codes, scales)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    if x.dtype == torch.bfloat16:
+        dt = IN_BF16
+    elif x.dtype == torch.float32:
+        dt = IN_F32
+    else:
+        raise ValueError(f"unsupported input dtype {x.dtype}")
+    rows, cols = x.shape
+    if from_amax is None:
+        from_amax = global_scale is None
+    if global_scale is None:
+        global_scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=x.device)
+    st = load().nvfp4_quantize(_ptr(x), dt, rows, cols, x.stride(0), _ptr(codes), _ptr(scales),
+                               _ptr(global_scale), SCALE_FROM_AMAX if from_amax else SCALE_GIVEN,
+                               _stream(stream))
+    _check(st, "nvfp4_quantize")
+    return codes, scales, global_scale
+
+
+def gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, *, out_dtype=torch.float32,
+         out: torch.Tensor | None = None, k: int | None = None, stream=None):
+    """y[M, N] = RN32(g_a g_w) deq(A) deq(W)^T from NVFP4 A [M, K] and W [N, K]."""
+    _need_gpu(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, out)
+    M = a_codes.shape[0]
+    N = w_codes.shape[0]
+    K = a_codes.shape[1] * 2 if k is None else k
+    if w_codes.shape[1] * 2 != K or a_scales.shape != (M, K // 16) or w_scales.shape != (N, K // 16):
+        raise ValueError("operand shapes disagree")
+    for t in (a_codes, a_scales, w_codes, w_scales):
+        if not t.is_contiguous() or t.dtype != torch.uint8:
+            raise ValueError("codes and scales must be contiguous uint8")
+    od = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[out_dtype]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    if out.dtype != out_dtype or out.stride(1) != 1:
+        raise ValueError("out must have unit column stride and dtype out_dtype")
+    lib = load()
+    ws_bytes = lib.nvfp4_gemm_workspace_size(M, N, K, od)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a_codes.device) if ws_bytes else None
+    st = lib.nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(a_gs), _ptr(w_codes), _ptr(w_scales),
+                        _ptr(w_gs), M, N, K, _ptr(out), od, out.stride(0), _ptr(ws), ws_bytes,
+                        _stream(stream))
+    _check(st, "nvfp4_gemm")
+    return out
+
+
+def harmonize_fused_scales(scales: torch.Tensor, module_gs: torch.Tensor, module_rows, k: int, *,
+                           shared_gs: torch.Tensor | None = None, counters: torch.Tensor | None = None,
+                           stream=None):
+    """Rescale (in place) the block scales of modules concatenated along N to
+    the shared tensor scale g* = max(module_gs).  Returns (shared_gs, counters)."""
+    _need_gpu(scales, module_gs, shared_gs, counters)
+    rows = (ctypes.c_int64 * len(module_rows))(*[int(r) for r in module_rows])
+    if shared_gs is None:
+        shared_gs = torch.empty(1, dtype=torch.float32, device=scales.device)
+    if counters is None:
+        counters = torch.zeros(2, dtype=torch.int32, device=scales.device)
+    st = load().nvfp4_harmonize_fused_scales(_ptr(scales), _ptr(module_gs), rows, len(module_rows), k,
+                                              _ptr(shared_gs), _ptr(counters), _stream(stream))
+    _check(st, "nvfp4_harmonize_fused_scales")
+    return shared_gs, counters

@@ -1,0 +1,122 @@
+// C ABI of the NVFP4 library: argument validation, then dispatch to the
+// kernel launchers.  Every check runs before the first HIP call, so a bad
+// argument never enqueues work (and the checks run on machines without a GPU).
+#include "../../include/nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+#include "nvfp4_internal.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+nvfp4_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return NVFP4_OK;
+  g_last_hip_error = (int32_t)e;
+  return NVFP4_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status_t nvfp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t cols,
+                              int64_t ldx, uint8_t* codes, uint8_t* scales,
+                              float* global_scale, int32_t mode, void* stream) {
+  try {
+    if (in_dtype != NVFP4_IN_F32 && in_dtype != NVFP4_IN_BF16) return NVFP4_ERR_DTYPE;
+    if (mode != NVFP4_SCALE_GIVEN && mode != NVFP4_SCALE_FROM_AMAX) return NVFP4_ERR_MODE;
+    if (rows < 0 || cols <= 0 || cols % 16 != 0 || ldx < cols) return NVFP4_ERR_SHAPE;
+    if (rows > INT64_MAX / (ldx > 0 ? ldx : 1) / 4) return NVFP4_ERR_SHAPE;
+    if (rows == 0) return NVFP4_OK;
+    if (!x || !codes || !scales || !global_scale) return NVFP4_ERR_NULL;
+    const int64_t esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
+    if (!aligned(x, 16) || (ldx * esize) % 16 != 0 || !aligned(codes, 8) || !aligned(global_scale, 4))
+      return NVFP4_ERR_ALIGN;
+    if ((rows * (cols / 16) + 255) / 256 > (int64_t)INT_MAX) return NVFP4_ERR_SHAPE;
+    return hip_status(nvfp4::launch_quantize(x, in_dtype == NVFP4_IN_BF16, rows, cols, ldx, codes,
+                                             scales, global_scale, mode == NVFP4_SCALE_FROM_AMAX,
+                                             (hipStream_t)stream));
+  } catch (...) {
+    return NVFP4_ERR_HIP;
+  }
+}
+
+size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t out_dtype) {
+  (void)M; (void)N; (void)K; (void)out_dtype;
+  return 0;
+}
+
+nvfp4_status_t nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                          const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
+                          int64_t M, int64_t N, int64_t K, void* y, int32_t out_dtype,
+                          int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_DTYPE;
+    if (M < 0 || N <= 0 || K <= 0 || K % 16 != 0 || ldy < N) return NVFP4_ERR_SHAPE;
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return NVFP4_ERR_SHAPE;
+    if (M == 0) return NVFP4_OK;
+    if (!a_codes || !a_scales || !a_gs || !w_codes || !w_scales || !w_gs || !y) return NVFP4_ERR_NULL;
+    if (!aligned(a_gs, 4) || !aligned(w_gs, 4) || !aligned(y, out_dtype == NVFP4_OUT_BF16 ? 2 : 4))
+      return NVFP4_ERR_ALIGN;
+    if (workspace_bytes < nvfp4_gemm_workspace_size(M, N, K, out_dtype)) return NVFP4_ERR_WORKSPACE;
+    (void)workspace;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles > (int64_t)INT_MAX) return NVFP4_ERR_SHAPE;
+    return hip_status(nvfp4::launch_gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, M, N, K, y,
+                                         out_dtype == NVFP4_OUT_BF16, ldy, (hipStream_t)stream));
+  } catch (...) {
+    return NVFP4_ERR_HIP;
+  }
+}
+
+nvfp4_status_t nvfp4_harmonize_fused_scales(uint8_t* scales, const float* module_gs,
+                                            const int64_t* module_rows, int32_t n_modules,
+                                            int64_t K, float* shared_gs, uint32_t* counters,
+                                            void* stream) {
+  try {
+    if (!scales || !module_gs || !module_rows || !shared_gs) return NVFP4_ERR_NULL;
+    if (n_modules < 1 || n_modules > nvfp4::kMaxModules) return NVFP4_ERR_SHAPE;
+    if (K <= 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;
+    int64_t total = 0;
+    for (int32_t i = 0; i < n_modules; ++i) {
+      if (module_rows[i] < 0 || module_rows[i] > INT64_MAX / 2 - total) return NVFP4_ERR_SHAPE;
+      total += module_rows[i];
+    }
+    if (total > INT64_MAX / (K / 16)) return NVFP4_ERR_SHAPE;
+    if (!aligned(module_gs, 4) || !aligned(shared_gs, 4) || (counters && !aligned(counters, 4)))
+      return NVFP4_ERR_ALIGN;
+    // the shared scale is written while module scales are still being read
+    const uintptr_t g0 = (uintptr_t)module_gs, g1 = g0 + 4u * (uintptr_t)n_modules;
+    const uintptr_t s0 = (uintptr_t)shared_gs;
+    if (s0 + 4 > g0 && s0 < g1) return NVFP4_ERR_ALIAS;
+    return hip_status(nvfp4::launch_harmonize(scales, module_gs, module_rows, n_modules, K, shared_gs,
+                                              counters, (hipStream_t)stream));
+  } catch (...) {
+    return NVFP4_ERR_HIP;
+  }
+}
+
+const char* nvfp4_status_string(int32_t status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "invalid shape";
+    case NVFP4_ERR_DTYPE: return "unknown dtype";
+    case NVFP4_ERR_MODE: return "unknown scale mode";
+    case NVFP4_ERR_ALIGN: return "misaligned pointer or row stride";
+    case NVFP4_ERR_WORKSPACE: return "workspace too small";
+    case NVFP4_ERR_HIP: return "HIP launch failed";
+    case NVFP4_ERR_ALIAS: return "output overlaps an input that is still being read";
+    default: return "unknown status";
+  }
+}
+
+int32_t nvfp4_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

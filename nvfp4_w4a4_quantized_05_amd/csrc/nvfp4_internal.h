@@ -1,0 +1,26 @@
+// Host-side launchers behind the C ABI.  Arguments are already validated by
+// nvfp4_api.cpp; each launcher only enqueues kernels and returns the launch
+// status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+hipError_t launch_quantize(const void* x, bool in_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                           uint8_t* codes, uint8_t* scales, float* global_scale, bool from_amax,
+                           hipStream_t stream);
+
+hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
+                       int64_t M, int64_t N, int64_t K, void* y, bool out_bf16, int64_t ldy,
+                       hipStream_t stream);
+
+constexpr int kMaxModules = 64;
+
+hipError_t launch_harmonize(uint8_t* scales, const float* module_gs, const int64_t* module_rows,
+                            int32_t n_modules, int64_t K, float* shared_gs, uint32_t* counters,
+                            hipStream_t stream);
+
+}  // namespace nvfp4

