@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark: one hybrid GDN layer's NVFP4 W4A4 projections at 32K-token prefill.
+
+One step is the whole hot path over one batch of 32,768 tokens:
+  quantize X      [32768 x 5120]  -> GEMM fused GDN in-projection (qkv|z|a|b,
+                                     N = 12384, harmonized tensor scale)
+  quantize X_out  [32768 x 4096]  -> GEMM GDN out-projection     (N = 5120)
+  quantize X_mlp  [32768 x 5120]  -> GEMM MLP gate/up            (N = 34816)
+  quantize X_d    [32768 x 17408] -> GEMM MLP down               (N = 5120)
+with bf16 inputs and bf16 outputs, all resident in HBM before timing starts.
+Activation tensor scales are static (calibrated once in setup with the
+library's amax mode), as in a calibrated W4A4 deployment; weights are
+quantized and the fused module scales harmonized in setup (offline work).
+
+Prints one JSON line.  `value` = GEMM TFLOP/s of the step (algorithmic
+2*M*N*K over the whole step time, quantize kernels included).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 W4A4 GEMM TFLOP/s at 32K-token prefill + quantize GB/s, % of roofline"
+PEAK_FP16_MFMA_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
+PEAK_HBM_GBPS = 8000.0           # MI355X HBM3E
+TOKENS = 32768
+QUANT_BYTES_PER_ELEM_BF16 = 2.0 + 0.5 + 1.0 / 16.0   # read bf16, write codes + scales
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gemm_gate_up_layer32k_hbm_counters.txt")
+GEMM_SOURCE = os.path.join(ROOT, "nvfp4_w4a4_quantized_05_amd", "csrc", "nvfp4_gemm.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tokens", type=int, default=TOKENS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="token rows in the CPU oracle sample")
+    return ap.parse_args()
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(per_launch_bytes_alg):
+    """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    text = open(PROFILE_COUNTERS).read()
+    m = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != source_hash(GEMM_SOURCE):
+        return None
+    return float(t.group(1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the NVFP4 projections shard over tokens or output columns without exchange; "
+              "see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nvfp4_w4a4_quantized_05_amd as nv
+    from workloads import CONFIGS, activations, normal_weights, stats
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cfg = CONFIGS["layer_32k"]
+    T = args.tokens
+    P = {p.name: p for p in cfg["projections"]}
+    seed = cfg["seed"]
+
+    # ---------------- setup (untimed): weights, harmonization, inputs -------
+    wq = {}
+    for i, p in enumerate(cfg["projections"]):
+        w = normal_weights(p.n, p.k, p.std, seed=seed * 100 + i, device=dev)
+        wq[p.name] = nv.quantize(w)
+        del w
+    fused = ["qkv", "z", "a", "b"]
+    in_codes = torch.cat([wq[n][0] for n in fused])
+    in_scales = torch.cat([wq[n][1] for n in fused])
+    module_gs = torch.cat([wq[n][2] for n in fused])
+    in_gs, harm_counters = nv.harmonize_fused_scales(in_scales, module_gs, [P[n].n for n in fused], 5120)
+    gemms = [  # (name, activation input index, codes, scales, gs, N, K)
+        ("in_proj", 0, in_codes, in_scales, in_gs, in_codes.shape[0], 5120),
+        ("out", 1, *wq["out"], P["out"].n, 4096),
+        ("gate_up", 2, *wq["gate_up"], P["gate_up"].n, 5120),
+        ("down", 3, *wq["down"], P["down"].n, 17408),
+    ]
+    kind = cfg["x"][0]
+    xs = [activations(kind, T, k, seed=seed * 10 + j, device=dev)
+          for j, k in enumerate((5120, 4096, 5120, 17408))]
+    x_stats = [stats(x) for x in xs]
+    # calibration: static activation tensor scales from the library's amax mode
+    calib = [nv.quantize(x)[2].clone() for x in xs]
+    qbuf = [(torch.empty((T, x.shape[1] // 2), dtype=torch.uint8, device=dev),
+             torch.empty((T, x.shape[1] // 16), dtype=torch.uint8, device=dev)) for x in xs]
+    ys = [torch.empty((T, g[5]), dtype=torch.bfloat16, device=dev) for g in gemms]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for gi, (name, xi, wc, ws, wg, n, k) in enumerate(gemms):
+            if ev is not None:
+                ev[gi][0].record(stream)
+            nv.quantize(xs[xi], calib[xi], from_amax=False, codes=qbuf[xi][0], scales=qbuf[xi][1])
+            if ev is not None:
+                ev[gi][1].record(stream)
+            nv.gemm(qbuf[xi][0], qbuf[xi][1], calib[xi], wc, ws, wg, out_dtype=torch.bfloat16, out=ys[gi])
+            if ev is not None:
+                ev[gi][2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in gemms] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / args.steps
+    q_ms = {g[0]: [] for g in gemms}
+    g_ms = {g[0]: [] for g in gemms}
+    for s in range(args.steps):
+        for gi, g in enumerate(gemms):
+            e = evs[s][gi]
+            q_ms[g[0]].append(e[0].elapsed_time(e[1]))
+            g_ms[g[0]].append(e[1].elapsed_time(e[2]))
+    flops = {g[0]: 2.0 * T * g[5] * g[6] for g in gemms}
+    total_flops = sum(flops.values())
+    qbytes = {g[0]: T * g[6] * QUANT_BYTES_PER_ELEM_BF16 for g in gemms}
+    per = {}
+    for g in gemms:
+        name = g[0]
+        gm = float(np.mean(g_ms[name]))
+        qm = float(np.mean(q_ms[name]))
+        per[name] = {"M": T, "N": g[5], "K": g[6], "gemm_ms": round(gm, 4),
+                     "gemm_tflops": round(flops[name] / gm / 1e9, 1),
+                     "gemm_frac_of_peak": round(flops[name] / gm / 1e9 / PEAK_FP16_MFMA_TFLOPS, 4),
+                     "quantize_ms": round(qm, 4),
+                     "quantize_gbps": round(qbytes[name] / qm / 1e6, 1)}
+    gemm_ms_total = sum(float(np.mean(g_ms[n])) for n in g_ms)
+    q_ms_total = sum(float(np.mean(q_ms[n])) for n in q_ms)
+    value = total_flops / (ms_step * 1e-3) / 1e12
+
+    # dominant kernel: the gate/up GEMM (half of the step's flops)
+    dom = per["gate_up"]
+    dom_alg_bytes = (T + dom["N"]) * dom["K"] * 0.5625 + T * dom["N"] * 2
+    achieved = flops["gate_up"] / (dom["gemm_ms"] * 1e-3) / 1e12
+    traffic = measured_traffic(dom_alg_bytes)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_MFMA_TFLOPS, 4),
+                "traffic": traffic, "kernel": "gemm gate/up 32768x34816x5120 (fp16 MFMA, fp32 acc)",
+                "algorithmic_bytes_per_launch": dom_alg_bytes}
+    qd = per["down"]  # largest activation: X_d [32768 x 17408]
+    q_ach = qbytes["down"] / (qd["quantize_ms"] * 1e-3) / 1e9
+    roofline_q = {"bound": "hbm", "achieved": round(q_ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                  "frac": round(q_ach / PEAK_HBM_GBPS, 4),
+                  "kernel": "quantize X_d 32768x17408 bf16 (2.5625 B/value)"}
+
+    # amax mode (dynamic activation scale) costs one more read of X
+    amax_ms = None
+    try:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g_tmp = torch.empty(1, dtype=torch.float32, device=dev)
+        e0.record(stream)
+        for _ in range(5):
+            nv.quantize(xs[3], g_tmp, from_amax=True, codes=qbuf[3][0], scales=qbuf[3][1])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        amax_ms = e0.elapsed_time(e1) / 5
+    except Exception:  # noqa: BLE001  (report, never fail the bench on this extra)
+        amax_ms = None
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "operands": "NVFP4 (E2M1 codes, E4M3 scale per 16, FP32 tensor scale); fp16 MFMA, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": f"layer_32k: one hybrid GDN layer's NVFP4 projections at {T} tokens "
+                               "(fused qkv|z|a|b 12384x5120, out 5120x4096, gate/up 34816x5120, "
+                               "down 5120x17408), bf16 in/out, static activation scales",
+                   "tokens": T, "gemm_tflop_per_step": round(total_flops / 1e12, 3),
+                   "activation_stats": x_stats},
+        "gemm_tflops": round(total_flops / (gemm_ms_total * 1e-3) / 1e12, 1),
+        "gemm_ms_per_step": round(gemm_ms_total, 4),
+        "quantize_ms_per_step": round(q_ms_total, 4),
+        "quantize_gbps": round(sum(qbytes.values()) / (q_ms_total * 1e-3) / 1e9, 1),
+        "quantize_amax_mode_ms_X_d": round(amax_ms, 4) if amax_ms else None,
+        "per_projection": per,
+        "harmonize_counters": [int(v) for v in harm_counters.cpu().tolist()],
+        "roofline": roofline,
+        "roofline_quantize": roofline_q,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_rows, xs, gemms, wq, fused, P, seed)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(rows, xs, gemms, wq, fused, P, seed):
+    """The CPU oracle (oracle/nvfp4_ref.py, untuned) timed on this host on a
+    bounded sample of the same step: the first `rows` tokens of every input,
+    and 1/8 of every projection's output features.  Weights for the sample are
+    quantized by the oracle beforehand (offline work, untimed)."""
+    import numpy as np
+    import torch
+
+    from oracle import nvfp4_ref as ref
+    from workloads import normal_weights
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    frac = 8
+    samples = []
+    for (name, xi, *_rest, n, k) in gemms:
+        cols = []
+        if name == "in_proj":
+            for mod in fused:
+                i = [p.name for p in P.values()].index(mod)
+                p = P[mod]
+                w = normal_weights(p.n, p.k, p.std, seed=seed * 100 + i, device="cpu")
+                cols.append(ref.quantize(w[: max(1, p.n // frac)].numpy(), g=ref.global_scale(w.numpy())))
+            wc = np.concatenate([c[0] for c in cols])
+            ws_list = [c[1] for c in cols]
+            hs, hg, _, _ = ref.harmonize_ref(ws_list, [c[2] for c in cols])
+            wqs = (wc, hs, hg)
+        else:
+            i = [p.name for p in P.values()].index(name)
+            p = P[name]
+            w = normal_weights(p.n, p.k, p.std, seed=seed * 100 + i, device="cpu")
+            wqs = ref.quantize(w[: p.n // frac].numpy(), g=ref.global_scale(w.numpy()))
+        x = xs[xi][:rows].float().cpu().numpy()
+        samples.append((x, wqs))
+    t0 = time.perf_counter()
+    flops = 0.0
+    for x, (wc, ws, wg) in samples:
+        a = ref.quantize(x)
+        ref.gemm_ref(*a, wc, ws, wg)
+        flops += 2.0 * x.shape[0] * wc.shape[0] * x.shape[1]
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "host_cpus": os.cpu_count(), "kind": "oracle",
+            "sample": f"first {rows} of {TOKENS} tokens of each input and 1/{frac} of each projection's "
+                      f"output features: {flops / 1e9:.1f} GFLOP + {sum(s[0].size for s in samples) / 1e6:.1f}M "
+                      f"values quantized in {dt:.1f} s (fp64 numpy oracle, quantize + GEMM + |a*w| sums)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -27,6 +27,8 @@
 //    always sit inside one 16-value block, i.e. one scale.
 //  * The RN32(g_a g_w) multiply and the fp32 or bf16 (RNE) conversion happen
 //    in the epilogue, straight from the accumulators.
+#include <type_traits>
+
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -230,24 +232,37 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(
       w_sc[j] = *reinterpret_cast<const uint32_t*>(&ws_lds[buf][row * kScaleBytes + half * 4]);
     }
 
+    // Software pipeline over the 8 MFMA k-steps of this K tile: the operands
+    // of step kk+1 are dequantized (VALU) while the MFMAs of step kk run,
+    // and the scheduler is asked to alternate one MFMA with a few VALU ops so
+    // that in-order issue never parks the VALU work behind a queue of MFMAs.
+    half8_t af[2][FM], wf[2][FN];
+    auto dequant_step = [&](int kk, int slot) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[slot][i] = dequant8(a_raw[i][kk >> 2][kk & 3], scale_pair((a_sc[i] >> (8 * (kk >> 1))) & 0xFFu));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        wf[slot][j] = dequant8(w_raw[j][kk >> 2][kk & 3], scale_pair((w_sc[j] >> (8 * (kk >> 1))) & 0xFFu));
+    };
+    dequant_step(0, 0);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      half8_t af[FM], wf[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const uint32_t c = a_raw[i][kk >> 2][kk & 3];
-        af[i] = dequant8(c, scale_pair((a_sc[i] >> (8 * (kk >> 1))) & 0xFFu));
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint32_t c = w_raw[j][kk >> 2][kk & 3];
-        wf[j] = dequant8(c, scale_pair((w_sc[j] >> (8 * (kk >> 1))) & 0xFFu));
-      }
+      const int cur = kk & 1;
+      if (kk + 1 < 8) dequant_step(kk + 1, cur ^ 1);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], wf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][i], wf[cur][j], acc[i][j], 0, 0, 0);
+      if (kk + 1 < 8) {
+        constexpr int kValuPerMfma = (8 * (FM + FN) + FN * FM - 1) / (FM * FN);
+#pragma unroll
+        for (int g = 0; g < FM * FN; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);   // then VALU
+        }
+      }
     }
 
     if (ks + 1 < ksteps) store_step(buf ^ 1);
@@ -273,6 +288,311 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(
             reinterpret_cast<float*>(y)[(int64_t)row * ldy + col] = o;
           }
         }
+      }
+    }
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Direct global -> LDS copies (no VGPR staging): each lane's bytes land at
+// lds_base + lane * size, so one wave instruction fills a contiguous span.
+__device__ __forceinline__ void lds_copy16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_copy4(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds_base, 4, 0, 0);
+}
+
+// Buffer-resource variant: base and size in SGPRs, a 32-bit per-lane offset
+// and a wave-uniform offset.  Offsets past the resource size read zeros.
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_copy4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 4, voff, soff, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// XOR swizzle of the four 16-byte chunks of a 64-byte LDS row: the 32 rows
+// read by one fragment load then hit distinct bank groups in every 8- and
+// 16-lane phase of ds_read_b128.
+__device__ __forceinline__ int chunk_swizzle(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+// Streaming kernel for the large shapes (K % 128 == 0, aligned operands).
+//
+// * 256 x 256 output tile per workgroup, 4 waves of 128 x 128 (4 x 4 blocks
+//   of 32 x 32), accumulators in AGPRs.
+// * K tiles of 128 values stream through a STAGES-deep LDS ring filled by
+//   direct global -> LDS copies (no VGPR staging), STAGES K tiles ahead.
+// * Each K tile is consumed in two halves.  While the MFMAs of one half run,
+//   the LDS reads for the next half are in flight, and the one barrier per
+//   K tile sits between the halves: after it the slot just read can be
+//   refilled and the next K tile's first half read.  No wait on LDS or on
+//   memory is then exposed in steady state except the barrier itself.
+// * The MFMA takes W as its "A" operand and A as "B", so each lane's
+//   accumulators hold 4 consecutive output columns of one row: the epilogue
+//   stages rows in LDS with 8-byte writes and stores 16-byte row chunks.
+// Rows past M or N read a clamped (valid) row; their outputs are never stored.
+template <int STAGES, bool kOutBf16>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
+    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_gs,
+    int M, int N, int K, void* __restrict__ y, int64_t ldy) {
+  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FM = 4, FN = 4;
+  constexpr int kCodeBytes = BM * kRowBytes;          // 16 KiB per operand per stage
+  constexpr int kStageScaleBytes = BM * kScaleBytes;  // 2 KiB per operand per stage
+  constexpr int kStageBytes = 2 * kCodeBytes + 2 * kStageScaleBytes;
+  constexpr int kLoadsPerStage = 12;                  // vector-memory instructions per wave per stage
+  using out_t = typename std::conditional<kOutBf16, __bf16, float>::type;
+  constexpr int kEsz = sizeof(out_t);
+  constexpr int kStripRows = 16;                      // output rows staged per pass
+  constexpr int kStripRow = WN * kEsz + 16;           // staged row bytes (+16 against bank conflicts)
+  constexpr int kStripBytes = kStripRows * kStripRow;
+  static_assert(STAGES >= 3, "ring depth");
+  static_assert((STAGES - 1) * kLoadsPerStage < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStageBytes + 4 * kStripBytes];
+  uint8_t* const ring = smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wave_m = wave >> 1, wave_n = wave & 1;
+  const int r32 = lane & 31, half = lane >> 5;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int64_t row_bytes = K / 2, srow_bytes = K / 16;
+  const int ksteps = K / kBK;
+  const float alpha = (*a_gs) * (*w_gs);
+  const bool vec_ok = ((uintptr_t)y % 16 == 0) && ((ldy * kEsz) % 16 == 0);
+
+  // Per-lane copy offsets of the current tile (32-bit, within buffer
+  // resources whose size bounds every read).  Wave w copies rows
+  // [64w, 64w+64) of both operands: codes with 4 instructions of 16 rows x 4
+  // (swizzled) 16-byte chunks, scales with 2 instructions of 32 rows x 2
+  // dwords.  Rows past the operand are clamped to its last row.
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_codes, (int64_t)M * row_bytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_codes, (int64_t)N * row_bytes);
+  const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_scales, (int64_t)M * srow_bytes);
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(w_scales, (int64_t)N * srow_bytes);
+  uint32_t a_off[4], w_off[4], as_off[2], ws_off[2];
+  auto set_sources = [&](int m0, int n0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wave * 64 + 16 * i + (lane >> 2);
+      const int chunk = (lane & 3) ^ chunk_swizzle(row);
+      a_off[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)row_bytes + chunk * 16;
+      w_off[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)row_bytes + chunk * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = wave * 64 + 32 * i + (lane >> 1);
+      as_off[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)srow_bytes + (lane & 1) * 4;
+      ws_off[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)srow_bytes + (lane & 1) * 4;
+    }
+  };
+  auto issue_stage = [&](int ks, int slot) {
+    uint8_t* st = ring + slot * kStageBytes;
+    const uint32_t kc = (uint32_t)ks * kRowBytes, kscl = (uint32_t)ks * kScaleBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_copy16(ra, a_off[i], kc, st + (wave * 64 + 16 * i) * kRowBytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_copy16(rw, w_off[i], kc, st + kCodeBytes + (wave * 64 + 16 * i) * kRowBytes);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      lds_copy4(ras, as_off[i], kscl, st + 2 * kCodeBytes + (wave * 64 + 32 * i) * kScaleBytes);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      lds_copy4(rws, ws_off[i], kscl, st + 2 * kCodeBytes + kStageScaleBytes + (wave * 64 + 32 * i) * kScaleBytes);
+  };
+
+  // Fragment registers: raw[.][h] holds the 16 code bytes of K-tile half h
+  // (MFMA steps 4h .. 4h+3); sc holds the 4 block scales of the K tile.
+  u32x4_t a_raw[FM][2], w_raw[FN][2];
+  uint32_t a_sc[FM], w_sc[FN], a_sc_next[FM], w_sc_next[FN];
+  auto read_half = [&](int slot, int h, bool with_scales) {
+    const uint8_t* st = ring + slot * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = wave_m * WM + i * 32 + r32;
+      a_raw[i][h] = *reinterpret_cast<const u32x4_t*>(st + row * kRowBytes + 16 * ((2 * half + h) ^ chunk_swizzle(row)));
+      if (with_scales) a_sc_next[i] = *reinterpret_cast<const uint32_t*>(st + 2 * kCodeBytes + row * kScaleBytes + half * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = wave_n * WN + j * 32 + r32;
+      w_raw[j][h] = *reinterpret_cast<const u32x4_t*>(st + kCodeBytes + row * kRowBytes + 16 * ((2 * half + h) ^ chunk_swizzle(row)));
+      if (with_scales)
+        w_sc_next[j] = *reinterpret_cast<const uint32_t*>(st + 2 * kCodeBytes + kStageScaleBytes + row * kScaleBytes + half * 4);
+    }
+  };
+
+  half8_t af[2][FM], wf[2][FN];
+  auto dequant_step = [&](int kk, int slot) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      af[slot][i] = dequant8(a_raw[i][kk >> 2][kk & 3], scale_pair((a_sc[i] >> (8 * (kk >> 1))) & 0xFFu));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      wf[slot][j] = dequant8(w_raw[j][kk >> 2][kk & 3], scale_pair((w_sc[j] >> (8 * (kk >> 1))) & 0xFFu));
+  };
+
+
+  int tile_m, tile_n;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+  set_sources(m0, n0);
+  // The ring always holds STAGES copies in flight or landed.  Past the last
+  // K tile the copies repeat the last one into a slot nobody reads again,
+  // which keeps the loop body free of branches (one scheduling region, so
+  // copies and LDS reads can be interleaved with the matrix instructions).
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s) issue_stage(min(s, ksteps - 1), s);
+
+  floatx16_t acc[FN][FM];  // acc[j][i]: rows of W block j (output columns) x columns of A block i (output rows)
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+  auto mfma_step = [&](int cur) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[cur][j], af[cur][i], acc[j][i], 0, 0, 0);
+  };
+  // Issue order inside one MFMA step: each MFMA is followed by 4 VALU
+  // (dequantization of the next step) and optionally one copy and/or LDS read.
+  auto schedule = [&](int n_vmem, int n_ds) {
+#pragma unroll
+    for (int g = 0; g < FM * FN; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);    // VALU
+      if (g < n_vmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (copy)
+      if (g < n_ds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
+    }
+  };
+
+  // first K tile: wait for its copies, then read its first half + scales
+  wait_vmcnt<(STAGES - 1) * kLoadsPerStage>();
+  __builtin_amdgcn_s_barrier();
+  read_half(0, 0, true);
+
+  for (int ks = 0; ks < ksteps; ++ks) {
+    const int slot = ks % STAGES;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) a_sc[i] = a_sc_next[i];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) w_sc[j] = w_sc_next[j];
+    // phase 1: MFMA steps 0..3 from half 0 while half 1 of this K tile is read
+    dequant_step(0, 0);
+    read_half(slot, 1, false);
+    dequant_step(1, 1);
+    mfma_step(0);
+    schedule(0, FM + FN);
+#pragma unroll
+    for (int kk = 1; kk < 4; ++kk) {
+      dequant_step(kk + 1, (kk + 1) & 1);
+      mfma_step(kk & 1);
+      schedule(0, 0);
+    }
+    // mid-tile: K tile ks+1 has landed (own copies + barrier); the slot just
+    // read is refilled with K tile ks+STAGES (clamped)
+    wait_vmcnt<(STAGES - 2) * kLoadsPerStage>();
+    // a bare s_barrier: __syncthreads() would also wait for every copy in
+    // flight and drain the ring
+    __builtin_amdgcn_s_barrier();
+    issue_stage(min(ks + STAGES, ksteps - 1), slot);
+    read_half((ks + 1) % STAGES, 0, true);
+    // phase 2: MFMA steps 4..7 from half 1 while the next K tile's half 0 is read
+    dequant_step(5, 1);
+    mfma_step(0);
+    schedule(kLoadsPerStage, FM * FN);
+#pragma unroll
+    for (int kk = 5; kk < 8; ++kk) {
+      if (kk + 1 < 8) dequant_step(kk + 1, (kk + 1) & 1);
+      mfma_step(kk & 1);
+      if (kk + 1 < 8) schedule(0, 0);
+    }
+  }
+  wait_vmcnt<0>();  // the repeated copies past the last K tile
+  __syncthreads();  // every wave is done with the ring
+
+  {
+    // Epilogue.  Lane (r32, half) of block (j, i) holds, for output row
+    // m = m0 + 128 wave_m + 32 i + r32, the columns n0 + 128 wave_n + 32 j +
+    // 8 (v / 4) + 4 half + (v % 4), v = 0..15: four consecutive columns per
+    // group of 4 accumulators.  Rows go through LDS in strips of 16.
+    uint8_t* strip = smem + STAGES * kStageBytes + wave * kStripBytes;
+    constexpr int kChunksPerRow = WN * kEsz / 16;
+    constexpr int kChunkElems = 16 / kEsz;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {      // rows r32 in [16 sub, 16 sub + 16)
+        if ((r32 >> 4) == sub) {
+          uint8_t* rowp = strip + (r32 & 15) * kStripRow;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int col = j * 32 + g * 8 + half * 4;
+              if constexpr (kOutBf16) {
+                typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
+                bf4_t o;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) o[t] = (__bf16)(acc[j][i][4 * g + t] * alpha);
+                *reinterpret_cast<bf4_t*>(rowp + col * kEsz) = o;
+              } else {
+                floatx4_t o;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) o[t] = acc[j][i][4 * g + t] * alpha;
+                *reinterpret_cast<floatx4_t*>(rowp + col * kEsz) = o;
+              }
+            }
+        }
+        const int grow0 = m0 + wave_m * WM + i * 32 + sub * 16;
+        const int gcol0 = n0 + wave_n * WN;
+        constexpr int kQ = kStripRows * kChunksPerRow / 64;
+        u32x4_t d[kQ];
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+          const int id = q * 64 + lane;
+          d[q] = *reinterpret_cast<const u32x4_t*>(strip + (id / kChunksPerRow) * kStripRow + (id % kChunksPerRow) * 16);
+        }
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+          const int id = q * 64 + lane;
+          const int r = id / kChunksPerRow, c = id % kChunksPerRow;
+          const int grow = grow0 + r, gcol = gcol0 + c * kChunkElems;
+          if (grow < M) {
+            out_t* dst = reinterpret_cast<out_t*>(y) + (int64_t)grow * ldy + gcol;
+            if (vec_ok && gcol + kChunkElems <= N) {
+              __builtin_nontemporal_store(d[q], reinterpret_cast<u32x4_t*>(dst));
+            } else {
+              const out_t* e = reinterpret_cast<const out_t*>(&d[q]);
+              for (int t = 0; t < kChunkElems; ++t)
+                if (gcol + t < N) dst[t] = e[t];
+            }
+          }
+        }
+        // Wait until the stores above have read their data registers
+        // (expcnt) before the next strip's LDS reads may reuse them.  Without
+        // it, when the compiler places the store data in AGPRs, a later
+        // ds_read into the same AGPRs was seen to overwrite the data of a
+        // store still in flight (wrong rows in the output).
+        __builtin_amdgcn_s_waitcnt(0xCF0F);  // expcnt(0); vmcnt, lgkmcnt untouched
       }
     }
   }
@@ -310,9 +630,17 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   const bool aligned = (K % kBK == 0) && ((uintptr_t)a_codes % 16 == 0) && ((uintptr_t)w_codes % 16 == 0) &&
                        ((uintptr_t)a_scales % 8 == 0) && ((uintptr_t)w_scales % 8 == 0);
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles >= 512) {
-    return launch_tiles<256, 256, 128, 128>(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, M, N, K, y,
-                                            out_bf16, ldy, aligned, stream);
+  const bool fits32 = M * (K / 2) < ((int64_t)1 << 31) && N * (K / 2) < ((int64_t)1 << 31);
+  if (aligned && fits32 && big_tiles >= 256) {
+    constexpr int kStages = 3;
+    const dim3 grid((unsigned)big_tiles), block(256);
+    if (out_bf16)
+      gemm_stream_kernel<kStages, true><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs,
+                                                                   (int)M, (int)N, (int)K, y, ldy);
+    else
+      gemm_stream_kernel<kStages, false><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs,
+                                                                    (int)M, (int)N, (int)K, y, ldy);
+    return hipGetLastError();
   }
   return launch_tiles<128, 128, 64, 64>(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, M, N, K, y,
                                         out_bf16, ldy, aligned, stream);

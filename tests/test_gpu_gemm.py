@@ -83,6 +83,21 @@ def test_ragged_shapes(shape):
         assert_gemm_close(y, Y, S, f"ragged {shape} {dt}")
 
 
+@pytest.mark.parametrize("shape", [(4113, 4140, 1024), (4096, 4096, 256), (3000, 6000, 640)])
+def test_large_tile_kernel_with_ragged_edges(shape):
+    """Shapes large enough for the 256x256 streaming kernel, with M and N tails."""
+    need_gpu()
+    M, N, K = shape
+    print(f"[gemm parity] streaming kernel M={M} N={N} K={K}", flush=True)
+    x = activations("t3_outlier1pct", M, K, seed=7, device="cpu")
+    w = normal_weights(N, K, 0.02, seed=8, device="cpu")
+    aq, wq = ref.quantize(host_f32(x)), ref.quantize(w.numpy())
+    Y, S = ref.gemm_ref(*aq, *wq)
+    for dt in (torch.float32, torch.bfloat16):
+        y = _run(aq, wq, dt)
+        assert_gemm_close(y, Y, S, f"large {shape} {dt}")
+
+
 def test_unaligned_operand_pointers_take_generic_path():
     need_gpu()
     M, N, K = 40, 72, 256
