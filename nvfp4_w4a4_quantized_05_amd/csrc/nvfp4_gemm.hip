@@ -366,7 +366,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   uint8_t* const ring = smem;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int wave_m = wave >> 1, wave_n = wave & 1;
   const int r32 = lane & 31, half = lane >> 5;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -598,6 +599,196 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   }
 }
 
+// Decode kernel (M <= 64): bound by the weight stream, N x K x 0.5625 bytes.
+//
+// A workgroup owns 48 weight rows (three 16-row MFMA blocks; 256 workgroups
+// cover N = 12288, one per CU) and all M rows of A.  Its 4 waves split K
+// into quarters, and each wave streams its quarter of W and of A through a
+// private ring of R K tiles in LDS with direct global->LDS copies, R tiles
+// ahead (>= 100 KB in flight per CU, enough to cover HBM latency at full
+// bandwidth).  A wave reads only its own ring, so no barrier is needed
+// inside the loop; a wave's copies complete in issue order, so one vmcnt
+// wait per K tile suffices.  MFMA 16x16x32 f16 with W as the "A" operand:
+// each lane ends up with 4 consecutive output columns of one row.  The four
+// partial sums are added through LDS in a fixed order (deterministic).
+// MB16 = number of 16-row blocks of A (1, 2 or 4).
+template <int MB16, int R, bool kOutBf16>
+__global__ __launch_bounds__(256) void gemm_decode_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
+    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_gs,
+    int M, int N, int K, void* __restrict__ y, int64_t ldy) {
+  constexpr int NW = 48;                           // weight rows per workgroup
+  constexpr int MA = 16 * MB16;                    // A rows per workgroup (padded)
+  constexpr int kWCode = NW * kRowBytes;           // 3072 B
+  constexpr int kWScale = NW * kScaleBytes;        // 384 B
+  constexpr int kACode = MA * kRowBytes;
+  constexpr int kAScale = MA * kScaleBytes;
+  constexpr int kSlot = kWCode + kWScale + kACode + kAScale;
+  constexpr int kWScaleInstr = (kWScale + 255) / 256;
+  constexpr int kAScaleInstr = (kAScale + 255) / 256;
+  constexpr int kPerSlot = 3 + kWScaleInstr + MB16 + kAScaleInstr;  // copy instructions per K tile
+  static_assert((R - 1) * kPerSlot < 64, "vmcnt range");
+  static_assert(4 * R * kSlot <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * R * kSlot];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int n0 = blockIdx.x * NW;
+  const int64_t row_bytes = K / 2, srow_bytes = K / 16;
+  const int ksteps = K / kBK;
+  const int kq0 = (ksteps * wave) / 4, nk = (ksteps * (wave + 1)) / 4 - kq0;
+  uint8_t* const ring = smem + wave * R * kSlot;
+
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_codes, (int64_t)N * row_bytes);
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(w_scales, (int64_t)N * srow_bytes);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_codes, (int64_t)M * row_bytes);
+  const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_scales, (int64_t)M * srow_bytes);
+  // per-lane copy offsets (K tile 0 of the workgroup's rows)
+  uint32_t w_off[3], a_off[MB16], ws_off[kWScaleInstr], as_off[kAScaleInstr];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int row = 16 * i + (lane >> 2);
+    w_off[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)row_bytes + (((lane & 3) ^ chunk_swizzle(row)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < MB16; ++i) {
+    const int row = 16 * i + (lane >> 2);
+    a_off[i] = (uint32_t)min(row, M - 1) * (uint32_t)row_bytes + (((lane & 3) ^ chunk_swizzle(row)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < kWScaleInstr; ++i) {
+    const int d = 64 * i + lane;  // dword index: row d / 2, half d % 2
+    ws_off[i] = (uint32_t)min(n0 + d / 2, N - 1) * (uint32_t)srow_bytes + (d & 1) * 4;
+  }
+#pragma unroll
+  for (int i = 0; i < kAScaleInstr; ++i) {
+    const int d = 64 * i + lane;
+    as_off[i] = (uint32_t)min(d / 2, M - 1) * (uint32_t)srow_bytes + (d & 1) * 4;
+  }
+  auto issue = [&](int t, int slot) {  // K tile kq0 + t of this wave into ring slot
+    uint8_t* st = ring + slot * kSlot;
+    const uint32_t kc = (uint32_t)(kq0 + t) * kRowBytes, ksc = (uint32_t)(kq0 + t) * kScaleBytes;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) lds_copy16(rw, w_off[i], kc, st + i * 1024);
+#pragma unroll
+    for (int i = 0; i < kWScaleInstr; ++i)
+      if (64 * i + lane < kWScale / 4) lds_copy4(rws, ws_off[i], ksc, st + kWCode + i * 256);
+#pragma unroll
+    for (int i = 0; i < MB16; ++i) lds_copy16(ra, a_off[i], kc, st + kWCode + kWScale + i * 1024);
+#pragma unroll
+    for (int i = 0; i < kAScaleInstr; ++i)
+      if (64 * i + lane < kAScale / 4) lds_copy4(ras, as_off[i], ksc, st + kWCode + kWScale + kACode + i * 256);
+  };
+
+  floatx4_t acc[3][MB16];
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int b = 0; b < MB16; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[j][b][v] = 0.0f;
+
+  if (nk > 0) {
+#pragma unroll
+    for (int t = 0; t < R; ++t) issue(min(t, nk - 1), t);
+    for (int t0 = 0; t0 < nk; t0 += R) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int t = t0 + u;
+        if (t < nk) {
+          wait_vmcnt<(R - 1) * kPerSlot>();
+          const uint8_t* st = ring + u * kSlot;
+          u32x4_t wc[3], ac[MB16];
+          uint32_t wsd[3], asd[MB16];
+#pragma unroll
+          for (int j = 0; j < 3; ++j) {
+            const int row = 16 * j + r16;
+            wc[j] = *reinterpret_cast<const u32x4_t*>(st + row * kRowBytes + 16 * (kg ^ chunk_swizzle(row)));
+            wsd[j] = *reinterpret_cast<const uint32_t*>(st + kWCode + row * kScaleBytes + 4 * (kg >> 1));
+          }
+#pragma unroll
+          for (int b = 0; b < MB16; ++b) {
+            const int row = 16 * b + r16;
+            ac[b] = *reinterpret_cast<const u32x4_t*>(st + kWCode + kWScale + row * kRowBytes + 16 * (kg ^ chunk_swizzle(row)));
+            asd[b] = *reinterpret_cast<const uint32_t*>(st + kWCode + kWScale + kACode + row * kScaleBytes + 4 * (kg >> 1));
+          }
+          // Operands of step s+1 are dequantized into the other half of a
+          // double buffer while the MFMAs of step s run, one MFMA then a few
+          // VALU at a time.  An MFMA's source registers are therefore never
+          // rewritten until at least one more MFMA has issued: a VALU write
+          // to them right behind a 16x16x32 MFMA was seen to corrupt the
+          // MFMA's input for the upper 8 rows of its A operand.
+          half8_t wv[2][3], av[2][MB16];
+          auto deq = [&](int s, int slot_) {
+            const int sb = 8 * (2 * (kg & 1) + (s >> 1));  // this step's scale byte in the lane's dword
+#pragma unroll
+            for (int b = 0; b < MB16; ++b) av[slot_][b] = dequant8(ac[b][s], scale_pair((asd[b] >> sb) & 0xFFu));
+#pragma unroll
+            for (int j = 0; j < 3; ++j) wv[slot_][j] = dequant8(wc[j][s], scale_pair((wsd[j] >> sb) & 0xFFu));
+          };
+          deq(0, 0);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            if (s + 1 < 4) deq(s + 1, (s + 1) & 1);
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+              for (int b = 0; b < MB16; ++b)
+                acc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv[s & 1][j], av[s & 1][b], acc[j][b], 0, 0, 0);
+            if (s + 1 < 4) {
+#pragma unroll
+              for (int g = 0; g < 3 * MB16; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, (8 * (3 + MB16) + 3 * MB16 - 1) / (3 * MB16), 0);  // VALU
+              }
+            }
+          }
+          // this slot's LDS reads are complete (their data fed the MFMAs);
+          // refill it with K tile t + R (repeating the last one past the end)
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+          issue(min(t + R, nk - 1), u);
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // fixed-order sum of the 4 K quarters through LDS (the ring is free now)
+  float* red = reinterpret_cast<float*>(smem);  // [3 waves][3][MB16][4][64]
+  if (wave > 0) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int b = 0; b < MB16; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[(((wave - 1) * 3 + j) * MB16 + b) * 256 + v * 64 + lane] = acc[j][b][v];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const float alpha = (*a_gs) * (*w_gs);
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int b = 0; b < MB16; ++b) {
+        const int m = 16 * b + r16;
+        const int n = n0 + 16 * j + 4 * kg;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float t = acc[j][b][v];
+#pragma unroll
+          for (int w = 0; w < 3; ++w) t += red[((w * 3 + j) * MB16 + b) * 256 + v * 64 + lane];
+          if (m < M && n + v < N) {
+            const float o = t * alpha;
+            if constexpr (kOutBf16) reinterpret_cast<__bf16*>(y)[(int64_t)m * ldy + n + v] = (__bf16)o;
+            else reinterpret_cast<float*>(y)[(int64_t)m * ldy + n + v] = o;
+          }
+        }
+      }
+  }
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_tiles(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
                         const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int64_t M,
@@ -640,6 +831,24 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
     else
       gemm_stream_kernel<kStages, false><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs,
                                                                     (int)M, (int)N, (int)K, y, ldy);
+    return hipGetLastError();
+  }
+  if (aligned && fits32 && M <= 64) {
+    const dim3 grid((unsigned)((N + 47) / 48)), block(256);
+    const int m = (int)M, n = (int)N, k = (int)K;
+#define NVFP4_DECODE(MB, RR)                                                                                  \
+  do {                                                                                                         \
+    if (out_bf16)                                                                                              \
+      gemm_decode_kernel<MB, RR, true><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, \
+                                                                   w_gs, m, n, k, y, ldy);                     \
+    else                                                                                                       \
+      gemm_decode_kernel<MB, RR, false><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, \
+                                                                    w_gs, m, n, k, y, ldy);                    \
+  } while (0)
+    if (M <= 16) NVFP4_DECODE(1, 8);
+    else if (M <= 32) NVFP4_DECODE(2, 6);
+    else NVFP4_DECODE(4, 4);
+#undef NVFP4_DECODE
     return hipGetLastError();
   }
   return launch_tiles<128, 128, 64, 64>(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, M, N, K, y,
