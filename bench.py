@@ -44,8 +44,23 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--tokens", type=int, default=TOKENS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256, help="token rows in the CPU oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=6144, help="token rows in the CPU oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (HBM counter calibration) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE
+    counters of rocprofv3: 3 copies of 1 GiB."""
+    import torch
+    src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": 1 << 30, "copies": 3}), flush=True)
 
 
 def source_hash(path):
@@ -67,6 +82,9 @@ def measured_traffic(per_launch_bytes_alg):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(the NVFP4 projections shard over tokens or output columns without exchange; "

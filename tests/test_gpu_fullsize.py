@@ -1,0 +1,154 @@
+"""Full-size workloads, in the launch configuration the bench times, checked on
+samples the oracle can afford: every tensor is generated and quantized at its
+real shape on the GPU; the oracle computes the tensor scale from the whole
+tensor, re-quantizes sampled rows (bit-exact comparison) and computes sampled
+GEMM outputs (tolerance comparison).  Activation scales are calibrated with
+the amax mode and then applied as static scales, as in the bench."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_w4a4_quantized_05_amd as nv
+from oracle import nvfp4_ref as ref
+from tests.gpu_util import assert_codes_equal, assert_gemm_close, host_f32, need_gpu
+from workloads import CONFIGS, activations, normal_weights
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(n, count, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(n, size=min(count, n), replace=False).tolist())
+    pick |= {i for i in extra if 0 <= i < n}
+    return np.array(sorted(pick))
+
+
+def _quant_checked(t, rows_sel, what, static=False):
+    """GPU-quantize t (amax mode, or calibrate then static), check sampled rows
+    and the tensor scale against the oracle; returns (GPU quantized, oracle g)."""
+    if static:
+        g = nv.quantize(t)[2].clone()
+        q = nv.quantize(t, g, from_amax=False)
+    else:
+        q = nv.quantize(t)
+    torch.cuda.synchronize()
+    host = host_f32(t)
+    g_or = ref.global_scale(host)
+    assert float(q[2].item()) == float(g_or), what
+    oc, os_, _ = ref.quantize(host[rows_sel], g=g_or)
+    assert_codes_equal(q[0][rows_sel].cpu().numpy(), q[1][rows_sel].cpu().numpy(), oc, os_, what)
+    return q, g_or, host
+
+
+def _check_gemm(aq, a_host, g_a, wq, w_host, g_w, rows_sel, cols_sel, what, out_dtype=torch.bfloat16):
+    y = nv.gemm(*aq, *wq, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    oa = ref.quantize(a_host[rows_sel], g=g_a)
+    ow = ref.quantize(w_host[cols_sel], g=g_w)
+    Y, S = ref.gemm_ref(*oa, *ow)
+    got = y[torch.from_numpy(rows_sel).cuda()][:, torch.from_numpy(cols_sel).cuda()]
+    return assert_gemm_close(got, Y, S, what)
+
+
+@pytest.mark.parametrize("which", ["gate_up", "down"])
+def test_prefill_mlp_full_size(which):
+    need_gpu()
+    cfg = CONFIGS["prefill_mlp"]
+    T = cfg["rows"]
+    kind = cfg["x"][0]
+    p = {q.name: q for q in cfg["projections"]}[which]
+    idx = [q.name for q in cfg["projections"]].index(which)
+    print(f"[full size] prefill_mlp {which}: X[{T}x{p.k}] W[{p.n}x{p.k}]", flush=True)
+    x = activations(kind, T, p.k, seed=cfg["seed"] * 10 + idx, device="cuda")
+    w = normal_weights(p.n, p.k, p.std, seed=cfg["seed"] * 100 + idx, device="cuda")
+    rows = _sample(T, 48, 1, extra=(0, 1, 255, 256, T - 1))
+    cols = _sample(p.n, 192, 2, extra=(0, 255, 256, p.n - 1))
+    aq, g_a, xa = _quant_checked(x, rows, f"X {which}", static=True)
+    wq, g_w, wh = _quant_checked(w, cols, f"W {which}")
+    del x, w
+    r = _check_gemm(aq, xa, g_a, wq, wh, g_w, rows, cols, f"prefill {which}")
+    print(f"  max |err|/sum|a w| = {r:.2e}", flush=True)
+
+
+def test_layer_32k_full_size():
+    """The bench workload: fused GDN in-projection with harmonized module scales,
+    out-projection, MLP gate/up and down at 32768 tokens."""
+    need_gpu()
+    cfg = CONFIGS["layer_32k"]
+    T = cfg["rows"]
+    kind = cfg["x"][0]
+    P = {q.name: q for q in cfg["projections"]}
+    names = [q.name for q in cfg["projections"]]
+    seed = cfg["seed"]
+    rows = _sample(T, 32, 3, extra=(0, T - 1))
+    wq, wh, wg = {}, {}, {}
+    for i, q in enumerate(cfg["projections"]):
+        w = normal_weights(q.n, q.k, q.std, seed=seed * 100 + i, device="cuda")
+        wq[q.name] = nv.quantize(w)
+        wh[q.name] = host_f32(w)
+        wg[q.name] = ref.global_scale(wh[q.name])
+        assert float(wq[q.name][2].item()) == float(wg[q.name])
+        del w
+    # fused in-projection: concatenate, harmonize on the GPU and in the oracle
+    fused = ["qkv", "z", "a", "b"]
+    codes = torch.cat([wq[n][0] for n in fused])
+    scales = torch.cat([wq[n][1] for n in fused])
+    mgs = torch.cat([wq[n][2] for n in fused])
+    shared, counters = nv.harmonize_fused_scales(scales, mgs, [P[n].n for n in fused], 5120)
+    torch.cuda.synchronize()
+    oq = {n: ref.quantize(wh[n], g=wg[n]) for n in fused}      # oracle per-module quantization
+    hs, hg, n_inexact, n_sub = ref.harmonize_ref([oq[n][1] for n in fused], [wg[n] for n in fused])
+    assert np.array_equal(scales.cpu().numpy(), hs)
+    assert float(shared.item()) == float(hg)
+    assert int(counters[0]) == n_inexact and int(counters[1]) == n_sub
+    in_codes_or = np.concatenate([oq[n][0] for n in fused])
+    assert np.array_equal(codes.cpu().numpy(), in_codes_or)
+    gemms = [("out", 1, wq["out"], wh["out"], wg["out"], 4096),
+             ("gate_up", 2, wq["gate_up"], wh["gate_up"], wg["gate_up"], 5120),
+             ("down", 3, wq["down"], wh["down"], wg["down"], 17408)]
+    # in-projection: harmonized fused weight
+    print(f"[full size] layer_32k in_proj: X[{T}x5120] W[{codes.shape[0]}x5120]", flush=True)
+    x = activations(kind, T, 5120, seed=seed * 10, device="cuda")
+    aq, g_a, xa = _quant_checked(x, rows, "layer X0", static=True)
+    del x
+    n = codes.shape[0]
+    cols = _sample(n, 160, 10, extra=(0, 8191, 8192, 12287, 12288, 12335, 12336, n - 1))
+    y = nv.gemm(*aq, codes, scales, shared, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    Y, S = ref.gemm_ref(*ref.quantize(xa[rows], g=g_a), in_codes_or[cols], hs[cols], hg)
+    got = y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]
+    r = assert_gemm_close(got, Y, S, "layer in_proj (harmonized)")
+    print(f"  max |err|/sum|a w| = {r:.2e}", flush=True)
+    del xa, y
+    for name, xi, wqq, whost, g_w, k in gemms:
+        print(f"[full size] layer_32k {name}: X[{T}x{k}] W[{whost.shape[0]}x{k}]", flush=True)
+        x = activations(kind, T, k, seed=seed * 10 + xi, device="cuda")
+        aq, g_a, xa = _quant_checked(x, rows, f"layer X{xi}", static=True)
+        del x
+        n = whost.shape[0]
+        cols = _sample(n, 160, 10 + xi, extra=(0, 255, 256, n - 1))
+        r = _check_gemm(aq, xa, g_a, wqq, whost, g_w, rows, cols, f"layer {name}")
+        print(f"  max |err|/sum|a w| = {r:.2e}", flush=True)
+        del xa
+
+
+def test_decode_quantize_then_gemm_chain():
+    """Decode shapes through the same two calls the decode loop makes."""
+    need_gpu()
+    cfg = CONFIGS["decode"]
+    p = cfg["projections"][0]
+    w = normal_weights(p.n, p.k, p.std, seed=cfg["seed"] * 100, device="cuda")
+    wq = nv.quantize(w)
+    wh = host_f32(w)
+    g_w = ref.global_scale(wh)
+    cols = np.arange(p.n)
+    ow = ref.quantize(wh, g=g_w)
+    for m in cfg["ms"]:
+        x = activations(cfg["x"][0], m, p.k, seed=cfg["seed"], device="cuda")
+        aq = nv.quantize(x)
+        y = nv.gemm(*aq, *wq, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        oa = ref.quantize(host_f32(x))
+        assert_codes_equal(aq[0], aq[1], oa[0], oa[1], f"decode X M={m}")
+        Y, S = ref.gemm_ref(*oa, *ow)
+        assert_gemm_close(y, Y, S, f"decode chain M={m}")
