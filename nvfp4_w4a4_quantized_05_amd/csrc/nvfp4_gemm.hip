@@ -39,6 +39,7 @@ constexpr int kBK = 128;              // K values per main-loop step
 constexpr int kRowBytes = kBK / 2;    // 64 code bytes per row per step
 constexpr int kLdsRow = kRowBytes + 16;  // padded LDS row stride: conflict-free 16-byte reads
 constexpr int kScaleBytes = kBK / 16;    // 8 scale bytes per row per step
+constexpr size_t kDecodeMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
 // fp16 pair (v, v) of an E4M3 scale byte times 2^-8.
 __device__ __forceinline__ uint32_t scale_pair(uint32_t byte) {
@@ -599,86 +600,105 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   }
 }
 
-// Decode kernel (M <= 64): bound by the weight stream, N x K x 0.5625 bytes.
+// Decode kernel (M <= 64, K % 256 == 0): bound by the weight stream,
+// N x K x 0.5625 bytes, which is read exactly once.
 //
-// A workgroup owns 48 weight rows (three 16-row MFMA blocks; 256 workgroups
-// cover N = 12288, one per CU) and all M rows of A.  Its 4 waves split K
-// into quarters, and each wave streams its quarter of W and of A through a
-// private ring of R K tiles in LDS with direct global->LDS copies, R tiles
-// ahead (>= 100 KB in flight per CU, enough to cover HBM latency at full
-// bandwidth).  A wave reads only its own ring, so no barrier is needed
-// inside the loop; a wave's copies complete in issue order, so one vmcnt
-// wait per K tile suffices.  MFMA 16x16x32 f16 with W as the "A" operand:
-// each lane ends up with 4 consecutive output columns of one row.  The four
-// partial sums are added through LDS in a fixed order (deterministic).
-// MB16 = number of 16-row blocks of A (1, 2 or 4).
-template <int MB16, int R, bool kOutBf16>
+// A workgroup owns 48 weight rows (three 16-row MFMA blocks; N = 12288 gives
+// 256 workgroups, one per CU) and all M rows of A; its 4 waves split K into
+// quarters of nt tiles of 256 values.  Codes go straight into registers, D
+// tiles ahead; only the scale bytes and the final reduction use LDS.
+//
+//  * One code load reads 8 rows x 128 contiguous bytes (lane L: row L % 8,
+//    16-byte chunk L / 8), the pattern that reaches full HBM read bandwidth;
+//    16 rows x 64 bytes per instruction loses about a quarter of it.
+//  * v_mfma_f32_16x16x32_f16 wants lane L to hold row L % 16 of its 16-row
+//    block.  Two loads X (rows 0-7) and Y (rows 8-15) are turned into that
+//    layout with two DPP row shifts by 8 lanes: R0 = X in lanes 0-7 of every
+//    16-lane row and Y shifted up in lanes 8-15 (chunk 2g for lane group g),
+//    R1 = X shifted down in lanes 0-7 and Y in lanes 8-15 (chunk 2g + 1).
+//    A is loaded and rearranged the same way (it stays in L2).
+//  * The scale bytes of the wave's whole K range (16 bytes per row per tile)
+//    are copied to LDS once, up front, in contiguous runs per row; read per
+//    tile, they cost no extra memory requests.
+//  * Rows >= M and rows >= N read zeros through the buffer bounds.
+//  * The four K-quarter partial sums are added through LDS in a fixed order
+//    (deterministic), then scaled by RN32(g_a g_w) and stored.
+// MB16 = number of 16-row blocks of A (1, 2 or 4); D = tiles in flight.
+template <int MB16>
+constexpr int decode_scale_rows() { return 48 + 16 * MB16; }
+
+template <int MB16, int D, bool kOutBf16>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_gs,
-    int M, int N, int K, void* __restrict__ y, int64_t ldy) {
-  constexpr int NW = 48;                           // weight rows per workgroup
-  constexpr int MA = 16 * MB16;                    // A rows per workgroup (padded)
-  constexpr int kWCode = NW * kRowBytes;           // 3072 B
-  constexpr int kWScale = NW * kScaleBytes;        // 384 B
-  constexpr int kACode = MA * kRowBytes;
-  constexpr int kAScale = MA * kScaleBytes;
-  constexpr int kSlot = kWCode + kWScale + kACode + kAScale;
-  constexpr int kWScaleInstr = (kWScale + 255) / 256;
-  constexpr int kAScaleInstr = (kAScale + 255) / 256;
-  constexpr int kPerSlot = 3 + kWScaleInstr + MB16 + kAScaleInstr;  // copy instructions per K tile
-  static_assert((R - 1) * kPerSlot < 64, "vmcnt range");
-  static_assert(4 * R * kSlot <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * R * kSlot];
+    int M, int N, int K, void* __restrict__ y, int64_t ldy, int nt_max) {
+  constexpr int NW = 48;  // weight rows per workgroup
+  constexpr int MA = 16 * MB16;
+  constexpr int kTileBytes = 128, kTileScales = 16;  // per row, per 256-value tile
+  constexpr int kLoads = 6 + 2 * MB16;               // code loads per tile
+  static_assert(D * kLoads < 64, "vmcnt range");
+  extern __shared__ __attribute__((aligned(16))) uint8_t dsmem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-  const int r16 = lane & 15, kg = lane >> 4;
+  const int q = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * NW;
-  const int64_t row_bytes = K / 2, srow_bytes = K / 16;
-  const int ksteps = K / kBK;
-  const int kq0 = (ksteps * wave) / 4, nk = (ksteps * (wave + 1)) / 4 - kq0;
-  uint8_t* const ring = smem + wave * R * kSlot;
+  const uint32_t row_bytes = (uint32_t)K / 2, srow_bytes = (uint32_t)K / 16;
+  const int kt = K / 256;
+  const int t0 = (kt * wave) / 4, nt = (kt * (wave + 1)) / 4 - t0;
+  const int run = nt * kTileScales;  // scale bytes per row in this wave's range
+  uint8_t* const wsl = dsmem + wave * decode_scale_rows<MB16>() * nt_max * kTileScales;  // [48 rows][run]
+  uint8_t* const asl = wsl + NW * run;                                                  // [MA rows][run]
 
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_codes, (int64_t)N * row_bytes);
   const __amdgpu_buffer_rsrc_t rws = make_rsrc(w_scales, (int64_t)N * srow_bytes);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_codes, (int64_t)M * row_bytes);
   const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_scales, (int64_t)M * srow_bytes);
-  // per-lane copy offsets (K tile 0 of the workgroup's rows)
-  uint32_t w_off[3], a_off[MB16], ws_off[kWScaleInstr], as_off[kAScaleInstr];
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int row = 16 * i + (lane >> 2);
-    w_off[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)row_bytes + (((lane & 3) ^ chunk_swizzle(row)) * 16);
+
+  // Scale runs to LDS: 16-byte unit u = row * nt + t lands at u * 16, so one
+  // instruction copies 64 consecutive units (whole row runs, contiguous).
+  if (nt > 0) {
+    const uint32_t inv = ((1u << 20) + nt - 1) / nt;  // u / nt == (u * inv) >> 20 for u * nt < 2^20
+    for (int i = 0; i * 64 < NW * nt; ++i) {
+      const uint32_t u = 64 * i + lane, row = (u * inv) >> 20, t = u - row * nt;
+      if (u < (uint32_t)(NW * nt))
+        lds_copy16(rws, (uint32_t)(n0 + row) * srow_bytes + (t0 + t) * kTileScales, 0, wsl + 64 * i * 16);
+    }
+    for (int i = 0; i * 64 < MA * nt; ++i) {
+      const uint32_t u = 64 * i + lane, row = (u * inv) >> 20, t = u - row * nt;
+      if (u < (uint32_t)(MA * nt))
+        lds_copy16(ras, row * srow_bytes + (t0 + t) * kTileScales, 0, asl + 64 * i * 16);
+    }
   }
+
+  // per-lane code offsets at tile 0 of this wave's K range
+  uint32_t w_off[6], a_off[2 * MB16];
 #pragma unroll
-  for (int i = 0; i < MB16; ++i) {
-    const int row = 16 * i + (lane >> 2);
-    a_off[i] = (uint32_t)min(row, M - 1) * (uint32_t)row_bytes + (((lane & 3) ^ chunk_swizzle(row)) * 16);
-  }
+  for (int i = 0; i < 6; ++i)  // block i / 2, rows 8 (i % 2) .. + 7
+    w_off[i] = (uint32_t)(n0 + 8 * i + (lane & 7)) * row_bytes + (uint32_t)(lane >> 3) * 16;
 #pragma unroll
-  for (int i = 0; i < kWScaleInstr; ++i) {
-    const int d = 64 * i + lane;  // dword index: row d / 2, half d % 2
-    ws_off[i] = (uint32_t)min(n0 + d / 2, N - 1) * (uint32_t)srow_bytes + (d & 1) * 4;
-  }
+  for (int i = 0; i < 2 * MB16; ++i)
+    a_off[i] = (uint32_t)(8 * i + (lane & 7)) * row_bytes + (uint32_t)(lane >> 3) * 16;
+
+  struct Tile {
+    u32x4_t w[6];
+    u32x4_t a[2 * MB16];
+  };
+  // Tile t0 + t of this wave.  Tiles past the wave's range (t >= nt) are
+  // read at an offset beyond every buffer's size: the loads return zeros
+  // without touching memory, and the zero tile adds nothing to the sums.
+  // That keeps the main loop branch-free, so the compiler can wait for each
+  // tile individually instead of draining every load in flight.
+  constexpr uint32_t kOutside = 0x80000000u;  // > any buffer size used here
+  auto load = [&](Tile& T, int t) {
+    const bool ok = t < nt;
+    const uint32_t kc = (uint32_t)(t0 + t) * kTileBytes;
 #pragma unroll
-  for (int i = 0; i < kAScaleInstr; ++i) {
-    const int d = 64 * i + lane;
-    as_off[i] = (uint32_t)min(d / 2, M - 1) * (uint32_t)srow_bytes + (d & 1) * 4;
-  }
-  auto issue = [&](int t, int slot) {  // K tile kq0 + t of this wave into ring slot
-    uint8_t* st = ring + slot * kSlot;
-    const uint32_t kc = (uint32_t)(kq0 + t) * kRowBytes, ksc = (uint32_t)(kq0 + t) * kScaleBytes;
+    for (int i = 0; i < 6; ++i)
+      T.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? w_off[i] + kc : kOutside, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 3; ++i) lds_copy16(rw, w_off[i], kc, st + i * 1024);
-#pragma unroll
-    for (int i = 0; i < kWScaleInstr; ++i)
-      if (64 * i + lane < kWScale / 4) lds_copy4(rws, ws_off[i], ksc, st + kWCode + i * 256);
-#pragma unroll
-    for (int i = 0; i < MB16; ++i) lds_copy16(ra, a_off[i], kc, st + kWCode + kWScale + i * 1024);
-#pragma unroll
-    for (int i = 0; i < kAScaleInstr; ++i)
-      if (64 * i + lane < kAScale / 4) lds_copy4(ras, as_off[i], ksc, st + kWCode + kWScale + kACode + i * 256);
+    for (int i = 0; i < 2 * MB16; ++i)
+      T.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off[i] + kc : kOutside, 0, 0);
   };
 
   floatx4_t acc[3][MB16];
@@ -689,74 +709,95 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[j][b][v] = 0.0f;
 
-  if (nk > 0) {
+  // X (rows 0-7) and Y (rows 8-15) of a 16-row block -> lane q holds row q:
+  // r0 = chunk 2g, r1 = chunk 2g + 1 of the tile.
+  auto to_mfma_rows = [](const u32x4_t& X, const u32x4_t& Y, u32x4_t& r0, u32x4_t& r1) {
 #pragma unroll
-    for (int t = 0; t < R; ++t) issue(min(t, nk - 1), t);
-    for (int t0 = 0; t0 < nk; t0 += R) {
+    for (int d = 0; d < 4; ++d) {
+      r0[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)X[d], (int)Y[d], 0x118, 0xF, 0xC, false);  // row_shr:8 -> lanes 8-15
+      r1[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)Y[d], (int)X[d], 0x108, 0xF, 0x3, false);  // row_shl:8 -> lanes 0-7
+    }
+  };
+
+  auto compute = [&](const Tile& T, int t) {
+    // scale dword of the lane (4 blocks: chunks 2g and 2g + 1); phantom
+    // tiles read the last real tile's scales (their codes are zero)
+    const int ts = min(t, nt - 1) * kTileScales + 4 * g;
+    uint32_t wsd[3], asd[MB16];
 #pragma unroll
-      for (int u = 0; u < R; ++u) {
-        const int t = t0 + u;
-        if (t < nk) {
-          wait_vmcnt<(R - 1) * kPerSlot>();
-          const uint8_t* st = ring + u * kSlot;
-          u32x4_t wc[3], ac[MB16];
-          uint32_t wsd[3], asd[MB16];
+    for (int j = 0; j < 3; ++j) wsd[j] = *reinterpret_cast<const uint32_t*>(wsl + (16 * j + q) * run + ts);
 #pragma unroll
-          for (int j = 0; j < 3; ++j) {
-            const int row = 16 * j + r16;
-            wc[j] = *reinterpret_cast<const u32x4_t*>(st + row * kRowBytes + 16 * (kg ^ chunk_swizzle(row)));
-            wsd[j] = *reinterpret_cast<const uint32_t*>(st + kWCode + row * kScaleBytes + 4 * (kg >> 1));
-          }
+    for (int b = 0; b < MB16; ++b) asd[b] = *reinterpret_cast<const uint32_t*>(asl + (16 * b + q) * run + ts);
+    u32x4_t wr[3][2], ar[MB16][2];
 #pragma unroll
-          for (int b = 0; b < MB16; ++b) {
-            const int row = 16 * b + r16;
-            ac[b] = *reinterpret_cast<const u32x4_t*>(st + kWCode + kWScale + row * kRowBytes + 16 * (kg ^ chunk_swizzle(row)));
-            asd[b] = *reinterpret_cast<const uint32_t*>(st + kWCode + kWScale + kACode + row * kScaleBytes + 4 * (kg >> 1));
-          }
-          // Operands of step s+1 are dequantized into the other half of a
-          // double buffer while the MFMAs of step s run, one MFMA then a few
-          // VALU at a time.  An MFMA's source registers are therefore never
-          // rewritten until at least one more MFMA has issued: a VALU write
-          // to them right behind a 16x16x32 MFMA was seen to corrupt the
-          // MFMA's input for the upper 8 rows of its A operand.
-          half8_t wv[2][3], av[2][MB16];
-          auto deq = [&](int s, int slot_) {
-            const int sb = 8 * (2 * (kg & 1) + (s >> 1));  // this step's scale byte in the lane's dword
+    for (int j = 0; j < 3; ++j) to_mfma_rows(T.w[2 * j], T.w[2 * j + 1], wr[j][0], wr[j][1]);
 #pragma unroll
-            for (int b = 0; b < MB16; ++b) av[slot_][b] = dequant8(ac[b][s], scale_pair((asd[b] >> sb) & 0xFFu));
+    for (int b = 0; b < MB16; ++b) to_mfma_rows(T.a[2 * b], T.a[2 * b + 1], ar[b][0], ar[b][1]);
+    // step s: chunk s / 4, dword s % 4; its scale is byte 2 (s / 4) + (s % 4) / 2
+    // of the lane's scale dword.  Operands of step s + 1 are dequantized into
+    // the other half of a double buffer while the MFMAs of step s run: a VALU
+    // write to a 16x16x32 MFMA's source registers right behind its issue was
+    // seen to corrupt the MFMA's input.
+    half8_t wv[2][3], av[2][MB16];
+    auto deq = [&](int s, int slot) {
+      const int c = s >> 2, dw = s & 3, sb = 8 * (2 * c + (dw >> 1));
 #pragma unroll
-            for (int j = 0; j < 3; ++j) wv[slot_][j] = dequant8(wc[j][s], scale_pair((wsd[j] >> sb) & 0xFFu));
-          };
-          deq(0, 0);
+      for (int b = 0; b < MB16; ++b) av[slot][b] = dequant8(ar[b][c][dw], scale_pair((asd[b] >> sb) & 0xFFu));
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            if (s + 1 < 4) deq(s + 1, (s + 1) & 1);
+      for (int j = 0; j < 3; ++j) wv[slot][j] = dequant8(wr[j][c][dw], scale_pair((wsd[j] >> sb) & 0xFFu));
+    };
+    deq(0, 0);
 #pragma unroll
-            for (int j = 0; j < 3; ++j)
+    for (int s = 0; s < 8; ++s) {
+      if (s + 1 < 8) deq(s + 1, (s + 1) & 1);
 #pragma unroll
-              for (int b = 0; b < MB16; ++b)
-                acc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv[s & 1][j], av[s & 1][b], acc[j][b], 0, 0, 0);
-            if (s + 1 < 4) {
+      for (int j = 0; j < 3; ++j)
 #pragma unroll
-              for (int g = 0; g < 3 * MB16; ++g) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, (8 * (3 + MB16) + 3 * MB16 - 1) / (3 * MB16), 0);  // VALU
-              }
-            }
-          }
-          // this slot's LDS reads are complete (their data fed the MFMAs);
-          // refill it with K tile t + R (repeating the last one past the end)
-          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-          issue(min(t + R, nk - 1), u);
+        for (int b = 0; b < MB16; ++b)
+          acc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv[s & 1][j], av[s & 1][b], acc[j][b], 0, 0, 0);
+      if (s + 1 < 8) {
+#pragma unroll
+        for (int i = 0; i < 3 * MB16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                             // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, (8 * (3 + MB16) + 3 * MB16 - 1) / (3 * MB16), 0);  // VALU
         }
       }
     }
-  }
-  wait_vmcnt<0>();
-  __syncthreads();
+  };
 
-  // fixed-order sum of the 4 K quarters through LDS (the ring is free now)
-  float* red = reinterpret_cast<float*>(smem);  // [3 waves][3][MB16][4][64]
+  {
+    Tile ring[D];
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      load(ring[u], u);
+      __builtin_amdgcn_sched_barrier(0);  // issue the tiles in order
+    }
+    // The scale copies were issued before the code loads and complete in
+    // order: once at most D * kLoads loads are outstanding they have landed.
+    wait_vmcnt<D * kLoads>();
+    __asm__ volatile("" ::: "memory");
+    const int n_full = nt / D;
+    for (int it = 0; it < n_full; ++it) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        compute(ring[u], it * D + u);
+        // keep the refill right here: left alone, the scheduler sinks all
+        // refills to the end of the loop body and every wait drains the queue
+        __builtin_amdgcn_sched_barrier(0);
+        load(ring[u], it * D + u + D);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // the last nt % D tiles are already in the ring
+#pragma unroll
+    for (int u = 0; u + 1 < D; ++u)
+      if (u < nt - n_full * D) compute(ring[u], n_full * D + u);
+  }
+
+  // fixed-order sum of the 4 K quarters through LDS (the scale area is free
+  // once every wave has passed the barrier)
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(dsmem);  // [3 waves][3][MB16][4][64]
   if (wave > 0) {
 #pragma unroll
     for (int j = 0; j < 3; ++j)
@@ -768,25 +809,63 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
   __syncthreads();
   if (wave == 0) {
     const float alpha = (*a_gs) * (*w_gs);
+    const bool vec_ok = (ldy % 4 == 0) && ((uintptr_t)y % 16 == 0);
 #pragma unroll
     for (int j = 0; j < 3; ++j)
 #pragma unroll
       for (int b = 0; b < MB16; ++b) {
-        const int m = 16 * b + r16;
-        const int n = n0 + 16 * j + 4 * kg;
+        const int m = 16 * b + q;
+        const int n = n0 + 16 * j + 4 * g;
+        floatx4_t o;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           float t = acc[j][b][v];
 #pragma unroll
           for (int w = 0; w < 3; ++w) t += red[((w * 3 + j) * MB16 + b) * 256 + v * 64 + lane];
-          if (m < M && n + v < N) {
-            const float o = t * alpha;
-            if constexpr (kOutBf16) reinterpret_cast<__bf16*>(y)[(int64_t)m * ldy + n + v] = (__bf16)o;
-            else reinterpret_cast<float*>(y)[(int64_t)m * ldy + n + v] = o;
+          o[v] = t * alpha;
+        }
+        if (m < M) {
+          if constexpr (kOutBf16) {
+            __bf16* dst = reinterpret_cast<__bf16*>(y) + (int64_t)m * ldy + n;
+            if (vec_ok && n + 3 < N) {
+              typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+              bf16x4_t h;
+#pragma unroll
+              for (int v = 0; v < 4; ++v) h[v] = (__bf16)o[v];
+              *reinterpret_cast<bf16x4_t*>(dst) = h;
+            } else {
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                if (n + v < N) dst[v] = (__bf16)o[v];
+            }
+          } else {
+            float* dst = reinterpret_cast<float*>(y) + (int64_t)m * ldy + n;
+            if (vec_ok && n + 3 < N) {
+              *reinterpret_cast<floatx4_t*>(dst) = o;
+            } else {
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                if (n + v < N) dst[v] = o[v];
+            }
           }
         }
       }
   }
+}
+
+// Dynamic LDS above 64 KiB has to be allowed per kernel before the launch.
+bool allow_lds(const void* fn, size_t bytes) {
+  if (bytes <= 64 * 1024) return true;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess;
+}
+
+// LDS bytes of a decode launch: the per-wave scale runs, or the reduction
+// buffer if larger.
+template <int MB16>
+size_t decode_lds_bytes(int nt_max) {
+  const size_t scales = (size_t)4 * decode_scale_rows<MB16>() * nt_max * 16;
+  const size_t red = (size_t)3 * 3 * MB16 * 4 * 64 * sizeof(float);
+  return scales > red ? scales : red;
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -833,23 +912,32 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
                                                                     (int)M, (int)N, (int)K, y, ldy);
     return hipGetLastError();
   }
-  if (aligned && fits32 && M <= 64) {
+  // decode: buffer offsets of rows up to N + 47 must stay below 2^31, and
+  // the scale runs of the longest K quarter must fit in LDS
+  const bool fits_decode = (N + 64) * (K / 2) < ((int64_t)1 << 31) && M * (K / 2) < ((int64_t)1 << 31);
+  if (aligned && fits_decode && M <= 64 && K % 256 == 0) {
+    const int nt_max = (int)((K / 256 + 3) / 4);
     const dim3 grid((unsigned)((N + 47) / 48)), block(256);
     const int m = (int)M, n = (int)N, k = (int)K;
-#define NVFP4_DECODE(MB, RR)                                                                                  \
-  do {                                                                                                         \
-    if (out_bf16)                                                                                              \
-      gemm_decode_kernel<MB, RR, true><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, \
-                                                                   w_gs, m, n, k, y, ldy);                     \
-    else                                                                                                       \
-      gemm_decode_kernel<MB, RR, false><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, \
-                                                                    w_gs, m, n, k, y, ldy);                    \
+#define NVFP4_DECODE(MB, DD)                                                                                   \
+  do {                                                                                                          \
+    const size_t lds = decode_lds_bytes<MB>(nt_max);                                                            \
+    const void* fn = out_bf16 ? (const void*)gemm_decode_kernel<MB, DD, true>                                   \
+                              : (const void*)gemm_decode_kernel<MB, DD, false>;                                 \
+    if (lds <= kDecodeMaxLds && allow_lds(fn, lds)) {                                                           \
+      if (out_bf16)                                                                                             \
+        gemm_decode_kernel<MB, DD, true><<<grid, block, lds, stream>>>(a_codes, a_scales, a_gs, w_codes,        \
+                                                                       w_scales, w_gs, m, n, k, y, ldy, nt_max); \
+      else                                                                                                      \
+        gemm_decode_kernel<MB, DD, false><<<grid, block, lds, stream>>>(a_codes, a_scales, a_gs, w_codes,       \
+                                                                        w_scales, w_gs, m, n, k, y, ldy, nt_max); \
+      return hipGetLastError();                                                                                 \
+    }                                                                                                           \
   } while (0)
-    if (M <= 16) NVFP4_DECODE(1, 8);
-    else if (M <= 32) NVFP4_DECODE(2, 6);
-    else NVFP4_DECODE(4, 4);
+    if (M <= 16) NVFP4_DECODE(1, 3);
+    else if (M <= 32) NVFP4_DECODE(2, 3);
+    else NVFP4_DECODE(4, 2);
 #undef NVFP4_DECODE
-    return hipGetLastError();
   }
   return launch_tiles<128, 128, 64, 64>(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, M, N, K, y,
                                         out_bf16, ldy, aligned, stream);

@@ -98,6 +98,23 @@ def test_large_tile_kernel_with_ragged_edges(shape):
         assert_gemm_close(y, Y, S, f"large {shape} {dt}")
 
 
+@pytest.mark.parametrize("shape", [(64, 100, 17408), (3, 49, 17408), (20, 96, 768), (33, 48, 2560),
+                                   (16, 12288, 4096)])
+def test_decode_kernel_k_splits(shape):
+    """M <= 64 with K % 256 == 0 takes the decode kernel: K quarters of 0..17
+    tiles, full and partial refill rounds, scale runs above 64 KiB of LDS."""
+    need_gpu()
+    M, N, K = shape
+    print(f"[gemm parity] decode kernel M={M} N={N} K={K}", flush=True)
+    x = activations("t3_outlier1pct", M, K, seed=M + K, device="cpu")
+    w = normal_weights(N, K, 0.02, seed=N + K, device="cpu")
+    aq, wq = ref.quantize(host_f32(x)), ref.quantize(w.numpy())
+    Y, S = ref.gemm_ref(*aq, *wq)
+    for dt in (torch.float32, torch.bfloat16):
+        y = _run(aq, wq, dt)
+        assert_gemm_close(y, Y, S, f"decode {shape} {dt}")
+
+
 def test_unaligned_operand_pointers_take_generic_path():
     need_gpu()
     M, N, K = 40, 72, 256
