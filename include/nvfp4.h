@@ -125,6 +125,39 @@ NVFP4_API nvfp4_status_t nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_sca
                           int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nvfp4_gemm_segmented -- one GEMM over modules concatenated along N, each
+ * keeping its own tensor scale: output columns of module i are
+ * RN32(g_a g_i) * deq(A) * deq(W_i)^T, where deq leaves out the tensor scale.
+ * This serves a fused projection (the GDN in-projection: qkv, z and the
+ * small a and b gate projections) with exactly the per-module result, with
+ * no rescaling of block scales (cctest.ai article "Why Gated DeltaNet Holds
+ * Up Under 4-Bit Quantization", "Main findings", last bullet, and LIT-800
+ * "Standing in the anthology": a fused kernel that applies one module's
+ * tensor scale to all of them mis-scales the others).  The pages repair the
+ * mismatch in the checkpoint instead (nvfp4_harmonize_fused_scales); this
+ * call is the alternative that moves the per-module scale to the epilogue.
+ *
+ *   a_codes, a_scales, a_gs   as for nvfp4_gemm
+ *   w_codes, w_scales         device, the modules' weights concatenated
+ *                             along N, each quantized with its own g_i
+ *   module_gs                 device, n_modules floats g_i
+ *   module_rows               HOST, n_modules row counts (each >= 0);
+ *                             N = their sum, 0 < N <= INT_MAX
+ *   n_modules                 1 .. 64
+ *   M, K, y, out_dtype, ldy, workspace, workspace_bytes, stream
+ *                             as for nvfp4_gemm
+ * Same kernels, accuracy and determinism as nvfp4_gemm; nvfp4_gemm is the
+ * case n_modules = 1.  NVFP4_ERR_NULL if module_rows is NULL; other errors as
+ * for nvfp4_gemm.
+ */
+NVFP4_API nvfp4_status_t nvfp4_gemm_segmented(const uint8_t* a_codes, const uint8_t* a_scales,
+                                              const float* a_gs, const uint8_t* w_codes,
+                                              const uint8_t* w_scales, const float* module_gs,
+                                              const int64_t* module_rows, int32_t n_modules, int64_t M,
+                                              int64_t K, void* y, int32_t out_dtype, int64_t ldy,
+                                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * nvfp4_harmonize_fused_scales -- re-express the block scales of modules
  * that are concatenated along N into one fused weight, each quantized with
  * its own tensor scale g_i, under one shared tensor scale g* = max_i g_i

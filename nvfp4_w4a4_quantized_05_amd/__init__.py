@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     Nvfp4Error,
     gemm,
+    gemm_segmented,
     harmonize_fused_scales,
     load,
     quantize,

@@ -22,7 +22,7 @@ SCALE_GIVEN, SCALE_FROM_AMAX = 0, 1
 STATUS_NAMES = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_DTYPE",
                 4: "NVFP4_ERR_MODE", 5: "NVFP4_ERR_ALIGN", 6: "NVFP4_ERR_WORKSPACE",
                 7: "NVFP4_ERR_HIP", 8: "NVFP4_ERR_ALIAS"}
-EXPORTS = ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_harmonize_fused_scales",
+EXPORTS = ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_segmented", "nvfp4_harmonize_fused_scales",
            "nvfp4_gemm_workspace_size", "nvfp4_status_string", "nvfp4_last_hip_error")
 
 _lib = None
@@ -51,6 +51,9 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_quantize.restype = i32
     lib.nvfp4_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp, sz, vp]
     lib.nvfp4_gemm.restype = i32
+    lib.nvfp4_gemm_segmented.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(i64), i32, i64, i64, vp, i32,
+                                         i64, vp, sz, vp]
+    lib.nvfp4_gemm_segmented.restype = i32
     lib.nvfp4_harmonize_fused_scales.argtypes = [vp, vp, ctypes.POINTER(i64), i32, i64, vp, vp, vp]
     lib.nvfp4_harmonize_fused_scales.restype = i32
     lib.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64, i32]
@@ -141,6 +144,38 @@ def gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, *, out_dtype=torch.fl
                         _ptr(w_gs), M, N, K, _ptr(out), od, out.stride(0), _ptr(ws), ws_bytes,
                         _stream(stream))
     _check(st, "nvfp4_gemm")
+    return out
+
+
+def gemm_segmented(a_codes, a_scales, a_gs, w_codes, w_scales, module_gs, module_rows, *,
+                   out_dtype=torch.float32, out: torch.Tensor | None = None, k: int | None = None, stream=None):
+    """One GEMM over modules concatenated along N (module_rows rows each): the
+    columns of module i are RN32(g_a g_i) deq(A) deq(W_i)^T, g_i = module_gs[i]."""
+    _need_gpu(a_codes, a_scales, a_gs, w_codes, w_scales, module_gs, out)
+    rows = [int(r) for r in module_rows]
+    M = a_codes.shape[0]
+    N = w_codes.shape[0]
+    K = a_codes.shape[1] * 2 if k is None else k
+    if sum(rows) != N or module_gs.numel() != len(rows) or module_gs.dtype != torch.float32:
+        raise ValueError("module_rows must sum to the weight rows, one float32 scale per module")
+    if w_codes.shape[1] * 2 != K or a_scales.shape != (M, K // 16) or w_scales.shape != (N, K // 16):
+        raise ValueError("operand shapes disagree")
+    for t in (a_codes, a_scales, w_codes, w_scales):
+        if not t.is_contiguous() or t.dtype != torch.uint8:
+            raise ValueError("codes and scales must be contiguous uint8")
+    od = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[out_dtype]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    if out.dtype != out_dtype or out.stride(1) != 1:
+        raise ValueError("out must have unit column stride and dtype out_dtype")
+    lib = load()
+    ws_bytes = lib.nvfp4_gemm_workspace_size(M, N, K, od)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a_codes.device) if ws_bytes else None
+    host_rows = (ctypes.c_int64 * len(rows))(*rows)
+    st = lib.nvfp4_gemm_segmented(_ptr(a_codes), _ptr(a_scales), _ptr(a_gs), _ptr(w_codes), _ptr(w_scales),
+                                  _ptr(module_gs.contiguous()), host_rows, len(rows), M, K, _ptr(out), od,
+                                  out.stride(0), _ptr(ws), ws_bytes, _stream(stream))
+    _check(st, "nvfp4_gemm_segmented")
     return out
 
 

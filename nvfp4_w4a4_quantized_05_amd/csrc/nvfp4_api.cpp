@@ -21,6 +21,26 @@ nvfp4_status_t hip_status(hipError_t e) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Checks shared by nvfp4_gemm and nvfp4_gemm_segmented (the caller has
+// filled the column scale table), then the launch.
+nvfp4_status_t gemm_checked(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                            const uint8_t* w_codes, const uint8_t* w_scales, const nvfp4::ColScales& cs,
+                            int64_t M, int64_t N, int64_t K, void* y, int32_t out_dtype, int64_t ldy,
+                            size_t workspace_bytes, void* stream) {
+  if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_DTYPE;
+  if (M < 0 || N <= 0 || K <= 0 || K % 16 != 0 || ldy < N) return NVFP4_ERR_SHAPE;
+  if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return NVFP4_ERR_SHAPE;
+  if (M == 0) return NVFP4_OK;
+  if (!a_codes || !a_scales || !a_gs || !w_codes || !w_scales || !cs.gs || !y) return NVFP4_ERR_NULL;
+  if (!aligned(a_gs, 4) || !aligned(cs.gs, 4) || !aligned(y, out_dtype == NVFP4_OUT_BF16 ? 2 : 4))
+    return NVFP4_ERR_ALIGN;
+  if (workspace_bytes < nvfp4_gemm_workspace_size(M, N, K, out_dtype)) return NVFP4_ERR_WORKSPACE;
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  if (tiles > (int64_t)INT_MAX) return NVFP4_ERR_SHAPE;
+  return hip_status(nvfp4::launch_gemm(a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y,
+                                       out_dtype == NVFP4_OUT_BF16, ldy, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -57,19 +77,36 @@ nvfp4_status_t nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
                           int64_t M, int64_t N, int64_t K, void* y, int32_t out_dtype,
                           int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
   try {
-    if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_DTYPE;
-    if (M < 0 || N <= 0 || K <= 0 || K % 16 != 0 || ldy < N) return NVFP4_ERR_SHAPE;
-    if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return NVFP4_ERR_SHAPE;
-    if (M == 0) return NVFP4_OK;
-    if (!a_codes || !a_scales || !a_gs || !w_codes || !w_scales || !w_gs || !y) return NVFP4_ERR_NULL;
-    if (!aligned(a_gs, 4) || !aligned(w_gs, 4) || !aligned(y, out_dtype == NVFP4_OUT_BF16 ? 2 : 4))
-      return NVFP4_ERR_ALIGN;
-    if (workspace_bytes < nvfp4_gemm_workspace_size(M, N, K, out_dtype)) return NVFP4_ERR_WORKSPACE;
-    (void)workspace;
-    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    if (tiles > (int64_t)INT_MAX) return NVFP4_ERR_SHAPE;
-    return hip_status(nvfp4::launch_gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, M, N, K, y,
-                                         out_dtype == NVFP4_OUT_BF16, ldy, (hipStream_t)stream));
+    nvfp4::ColScales cs{};
+    cs.gs = w_gs;
+    cs.n = 1;
+    cs.end[0] = (N > 0 && N <= INT_MAX) ? (int)N : 0;  // out-of-range N fails the shape check
+    return gemm_checked(a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y, out_dtype, ldy,
+                        workspace_bytes, stream);
+  } catch (...) {
+    return NVFP4_ERR_HIP;
+  }
+}
+
+nvfp4_status_t nvfp4_gemm_segmented(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                                    const uint8_t* w_codes, const uint8_t* w_scales,
+                                    const float* module_gs, const int64_t* module_rows, int32_t n_modules,
+                                    int64_t M, int64_t K, void* y, int32_t out_dtype, int64_t ldy,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (!module_rows) return NVFP4_ERR_NULL;
+    if (n_modules < 1 || n_modules > nvfp4::kMaxModules) return NVFP4_ERR_SHAPE;
+    nvfp4::ColScales cs{};
+    cs.gs = module_gs;
+    cs.n = n_modules;
+    int64_t N = 0;
+    for (int32_t i = 0; i < n_modules; ++i) {
+      if (module_rows[i] < 0 || module_rows[i] > (int64_t)INT_MAX - N) return NVFP4_ERR_SHAPE;
+      N += module_rows[i];
+      cs.end[i] = (int)N;
+    }
+    return gemm_checked(a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y, out_dtype, ldy,
+                        workspace_bytes, stream);
   } catch (...) {
     return NVFP4_ERR_HIP;
   }

@@ -77,6 +77,19 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = r / gsize;
 }
 
+// Column range of `col` in the per-column tensor scales: the number of
+// range ends at or below it (ends are non-decreasing).
+__device__ __forceinline__ int col_range(const ColScales& cs, int col) {
+  int s = 0;
+  for (int i = 0; i + 1 < cs.n; ++i) s += col >= cs.end[i] ? 1 : 0;
+  return s;
+}
+
+// RN32(g_a g_w) of output column `col`.
+__device__ __forceinline__ float col_alpha(float g_a, const ColScales& cs, int col) {
+  return g_a * cs.gs[col_range(cs, col)];
+}
+
 template <bool kAligned>
 __device__ __forceinline__ u32x4_t load_codes16(const uint8_t* row_ptr, int64_t byte_off, int64_t row_bytes,
                                                bool row_ok) {
@@ -126,7 +139,7 @@ __device__ __forceinline__ u32x2_t load_scales8(const uint8_t* row_ptr, int64_t 
 template <int BM, int BN, int WM, int WN, bool kAligned, bool kOutBf16>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
-    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_gs,
+    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const ColScales cs,
     int M, int N, int K, void* __restrict__ y, int64_t ldy) {
   constexpr int kWavesM = BM / WM, kWavesN = BN / WN;
   constexpr int kThreads = kWavesM * kWavesN * 64;
@@ -270,14 +283,15 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(
     __syncthreads();
   }
 
-  // epilogue: y = acc * RN32(g_a g_w)
-  const float alpha = (*a_gs) * (*w_gs);
+  // epilogue: y = acc * RN32(g_a g_w) with the column's g_w
+  const float g_a = *a_gs;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int col = n0 + wave_n * WN + j * 32 + r32;
       if (col >= N) continue;
+      const float alpha = col_alpha(g_a, cs, col);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = m0 + wave_m * WM + i * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
@@ -349,7 +363,7 @@ __device__ __forceinline__ int chunk_swizzle(int row) { return ((row >> 1) ^ (ro
 template <int STAGES, bool kOutBf16>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
-    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_gs,
+    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const ColScales cs,
     int M, int N, int K, void* __restrict__ y, int64_t ldy) {
   constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FM = 4, FN = 4;
   constexpr int kCodeBytes = BM * kRowBytes;          // 16 KiB per operand per stage
@@ -363,7 +377,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   constexpr int kStripBytes = kStripRows * kStripRow;
   static_assert(STAGES >= 3, "ring depth");
   static_assert((STAGES - 1) * kLoadsPerStage < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStageBytes + 4 * kStripBytes];
+  constexpr int kAlphaBytes = WN * 4;                 // per-wave column scale table
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStageBytes + 4 * kStripBytes + 4 * kAlphaBytes];
   uint8_t* const ring = smem;
 
   const int tid = threadIdx.x;
@@ -374,7 +389,6 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int64_t row_bytes = K / 2, srow_bytes = K / 16;
   const int ksteps = K / kBK;
-  const float alpha = (*a_gs) * (*w_gs);
   const bool vec_ok = ((uintptr_t)y % 16 == 0) && ((ldy * kEsz) % 16 == 0);
 
   // Per-lane copy offsets of the current tile (32-bit, within buffer
@@ -531,11 +545,27 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   wait_vmcnt<0>();  // the repeated copies past the last K tile
   __syncthreads();  // every wave is done with the ring
 
+  // Epilogue.  Lane (r32, half) of block (j, i) holds, for output row
+  // m = m0 + 128 wave_m + 32 i + r32, the columns n0 + 128 wave_n + 32 j +
+  // 8 (v / 4) + 4 half + (v % 4), v = 0..15: four consecutive columns per
+  // group of 4 accumulators.  Rows go through LDS in strips of 16.
+  // RN32(g_a g_w) of the wave's 128 columns goes to a small LDS table; each
+  // group of 4 columns reads its 4 values from there.  When one column range
+  // covers all 128 columns (every plain GEMM, and most tiles of a segmented
+  // one) the table holds one value, found with one lookup.
+  const float g_a = *a_gs;
+  const int c_first = n0 + wave_n * WN, c_last = min(c_first + WN, N) - 1;
+  const int s_first = col_range(cs, c_first);
+  float* const alpha_tab = reinterpret_cast<float*>(smem + STAGES * kStageBytes + 4 * kStripBytes) + wave * WN;
+  if (s_first == col_range(cs, c_last)) {
+    const float alpha = g_a * cs.gs[s_first];
+    alpha_tab[lane] = alpha;
+    alpha_tab[lane + 64] = alpha;
+  } else {
+    alpha_tab[lane] = col_alpha(g_a, cs, c_first + lane);
+    alpha_tab[lane + 64] = col_alpha(g_a, cs, c_first + lane + 64);
+  }
   {
-    // Epilogue.  Lane (r32, half) of block (j, i) holds, for output row
-    // m = m0 + 128 wave_m + 32 i + r32, the columns n0 + 128 wave_n + 32 j +
-    // 8 (v / 4) + 4 half + (v % 4), v = 0..15: four consecutive columns per
-    // group of 4 accumulators.  Rows go through LDS in strips of 16.
     uint8_t* strip = smem + STAGES * kStageBytes + wave * kStripBytes;
     constexpr int kChunksPerRow = WN * kEsz / 16;
     constexpr int kChunkElems = 16 / kEsz;
@@ -550,16 +580,17 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               const int col = j * 32 + g * 8 + half * 4;
+              const floatx4_t al = *reinterpret_cast<const floatx4_t*>(alpha_tab + col);
               if constexpr (kOutBf16) {
                 typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
                 bf4_t o;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) o[t] = (__bf16)(acc[j][i][4 * g + t] * alpha);
+                for (int t = 0; t < 4; ++t) o[t] = (__bf16)(acc[j][i][4 * g + t] * al[t]);
                 *reinterpret_cast<bf4_t*>(rowp + col * kEsz) = o;
               } else {
                 floatx4_t o;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) o[t] = acc[j][i][4 * g + t] * alpha;
+                for (int t = 0; t < 4; ++t) o[t] = acc[j][i][4 * g + t] * al[t];
                 *reinterpret_cast<floatx4_t*>(rowp + col * kEsz) = o;
               }
             }
@@ -630,7 +661,7 @@ constexpr int decode_scale_rows() { return 48 + 16 * MB16; }
 template <int MB16, int D, bool kOutBf16>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
-    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_gs,
+    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const ColScales cs,
     int M, int N, int K, void* __restrict__ y, int64_t ldy, int nt_max) {
   constexpr int NW = 48;  // weight rows per workgroup
   constexpr int MA = 16 * MB16;
@@ -808,7 +839,11 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
   }
   __syncthreads();
   if (wave == 0) {
-    const float alpha = (*a_gs) * (*w_gs);
+    // one tensor scale for the workgroup's 48 columns unless a column range
+    // ends inside them
+    const float g_a = *a_gs;
+    const int s_first = col_range(cs, n0), s_last = col_range(cs, min(n0 + NW, N) - 1);
+    const float alpha_u = g_a * cs.gs[s_first];
     const bool vec_ok = (ldy % 4 == 0) && ((uintptr_t)y % 16 == 0);
 #pragma unroll
     for (int j = 0; j < 3; ++j)
@@ -822,7 +857,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
           float t = acc[j][b][v];
 #pragma unroll
           for (int w = 0; w < 3; ++w) t += red[((w * 3 + j) * MB16 + b) * 256 + v * 64 + lane];
-          o[v] = t * alpha;
+          o[v] = t * (s_first == s_last ? alpha_u : col_alpha(g_a, cs, n + v));
         }
         if (m < M) {
           if constexpr (kOutBf16) {
@@ -870,7 +905,7 @@ size_t decode_lds_bytes(int nt_max) {
 
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_tiles(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
-                        const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int64_t M,
+                        const uint8_t* w_codes, const uint8_t* w_scales, const ColScales& cs, int64_t M,
                         int64_t N, int64_t K, void* y, bool out_bf16, int64_t ldy, bool aligned,
                         hipStream_t stream) {
   constexpr int kThreads = (BM / WM) * (BN / WN) * 64;
@@ -879,14 +914,14 @@ hipError_t launch_tiles(const uint8_t* a_codes, const uint8_t* a_scales, const f
   const int m = (int)M, n = (int)N, k = (int)K;
   if (aligned) {
     if (out_bf16)
-      gemm_kernel<BM, BN, WM, WN, true, true><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, m, n, k, y, ldy);
+      gemm_kernel<BM, BN, WM, WN, true, true><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, cs, m, n, k, y, ldy);
     else
-      gemm_kernel<BM, BN, WM, WN, true, false><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, m, n, k, y, ldy);
+      gemm_kernel<BM, BN, WM, WN, true, false><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, cs, m, n, k, y, ldy);
   } else {
     if (out_bf16)
-      gemm_kernel<BM, BN, WM, WN, false, true><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, m, n, k, y, ldy);
+      gemm_kernel<BM, BN, WM, WN, false, true><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, cs, m, n, k, y, ldy);
     else
-      gemm_kernel<BM, BN, WM, WN, false, false><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, m, n, k, y, ldy);
+      gemm_kernel<BM, BN, WM, WN, false, false><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, cs, m, n, k, y, ldy);
   }
   return hipGetLastError();
 }
@@ -894,7 +929,7 @@ hipError_t launch_tiles(const uint8_t* a_codes, const uint8_t* a_scales, const f
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
-                       const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const ColScales& cs,
                        int64_t M, int64_t N, int64_t K, void* y, bool out_bf16, int64_t ldy,
                        hipStream_t stream) {
   const bool aligned = (K % kBK == 0) && ((uintptr_t)a_codes % 16 == 0) && ((uintptr_t)w_codes % 16 == 0) &&
@@ -905,10 +940,10 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
     constexpr int kStages = 3;
     const dim3 grid((unsigned)big_tiles), block(256);
     if (out_bf16)
-      gemm_stream_kernel<kStages, true><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs,
+      gemm_stream_kernel<kStages, true><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, cs,
                                                                    (int)M, (int)N, (int)K, y, ldy);
     else
-      gemm_stream_kernel<kStages, false><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs,
+      gemm_stream_kernel<kStages, false><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, cs,
                                                                     (int)M, (int)N, (int)K, y, ldy);
     return hipGetLastError();
   }
@@ -927,10 +962,10 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
     if (lds <= kDecodeMaxLds && allow_lds(fn, lds)) {                                                           \
       if (out_bf16)                                                                                             \
         gemm_decode_kernel<MB, DD, true><<<grid, block, lds, stream>>>(a_codes, a_scales, a_gs, w_codes,        \
-                                                                       w_scales, w_gs, m, n, k, y, ldy, nt_max); \
+                                                                       w_scales, cs, m, n, k, y, ldy, nt_max); \
       else                                                                                                      \
         gemm_decode_kernel<MB, DD, false><<<grid, block, lds, stream>>>(a_codes, a_scales, a_gs, w_codes,       \
-                                                                        w_scales, w_gs, m, n, k, y, ldy, nt_max); \
+                                                                        w_scales, cs, m, n, k, y, ldy, nt_max); \
       return hipGetLastError();                                                                                 \
     }                                                                                                           \
   } while (0)
@@ -939,7 +974,7 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
     else NVFP4_DECODE(4, 2);
 #undef NVFP4_DECODE
   }
-  return launch_tiles<128, 128, 64, 64>(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, M, N, K, y,
+  return launch_tiles<128, 128, 64, 64>(a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y,
                                         out_bf16, ldy, aligned, stream);
 }
 

@@ -12,12 +12,22 @@ hipError_t launch_quantize(const void* x, bool in_bf16, int64_t rows, int64_t co
                            uint8_t* codes, uint8_t* scales, float* global_scale, bool from_amax,
                            hipStream_t stream);
 
+constexpr int kMaxModules = 64;
+
+// Tensor scales of the weight's output columns.  Column range s (s = 0 ..
+// n - 1) is [end[s - 1], end[s]) with end[-1] = 0 and end[n - 1] = N; its
+// tensor scale is gs[s] (device).  A plain GEMM is the case n = 1.  Passed
+// to the kernels by value (kernel arguments).
+struct ColScales {
+  const float* gs;
+  int n;
+  int end[kMaxModules];
+};
+
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
-                       const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const ColScales& cs,
                        int64_t M, int64_t N, int64_t K, void* y, bool out_bf16, int64_t ldy,
                        hipStream_t stream);
-
-constexpr int kMaxModules = 64;
 
 hipError_t launch_harmonize(uint8_t* scales, const float* module_gs, const int64_t* module_rows,
                             int32_t n_modules, int64_t K, float* shared_gs, uint32_t* counters,

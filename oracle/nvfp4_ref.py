@@ -208,6 +208,27 @@ def gemm_ref(a_codes, a_scales, g_a, w_codes, w_scales, g_w):
     return y, sabs
 
 
+def gemm_segmented_ref(a_codes, a_scales, g_a, w_codes, w_scales, module_gs, module_rows):
+    """One GEMM over modules concatenated along N in which every module keeps
+    its own tensor scale: the columns of module i are g_a g_i deq(A) deq(W_i)^T.
+    This is the per-module result that a fused projection must reproduce
+    ([CT] "Main findings", last bullet; [LIT] "Standing in the anthology"),
+    written as what it means: the per-module GEMMs side by side.
+
+    Returns (Y, Sabs) like gemm_ref."""
+    ys, ss = [], []
+    r0 = 0
+    for g_i, rows in zip(module_gs, module_rows):
+        sl = slice(r0, r0 + int(rows))
+        y, sabs = gemm_ref(a_codes, a_scales, g_a, w_codes[sl], w_scales[sl], np.float32(g_i))
+        ys.append(y)
+        ss.append(sabs)
+        r0 += int(rows)
+    if r0 != w_codes.shape[0]:
+        raise ValueError("module rows must add up to the weight rows")
+    return np.concatenate(ys, axis=1), np.concatenate(ss, axis=1)
+
+
 def harmonize_ref(scales_list, module_gs):
     """Bring per-module tensor scales of a fused projection to one shared scale.
 

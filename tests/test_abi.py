@@ -95,6 +95,33 @@ def test_gemm_rejects_bad_arguments(lib):
     assert lib.nvfp4_gemm_workspace_size(64, 12288, 5120, 0) == 0
 
 
+def gs_(lib, rows=(8, 0, 4), M=4, K=32, y=P16, od=0, ldy=12, ptrs=None, mgs=P16, n=None, host_rows=True):
+    p = ptrs or [P16] * 5
+    arr = (ctypes.c_int64 * max(len(rows), 1))(*rows) if host_rows else None
+    return lib.nvfp4_gemm_segmented(*p, mgs, arr, len(rows) if n is None else n, M, K, y, od, ldy,
+                                    None, 0, None)
+
+
+def test_gemm_segmented_rejects_bad_arguments(lib):
+    assert gs_(lib, host_rows=False) == NULL
+    assert gs_(lib, n=0) == SHAPE
+    assert gs_(lib, rows=tuple([1] * 65), ldy=65) == SHAPE
+    assert gs_(lib, rows=(8, -1, 4)) == SHAPE
+    assert gs_(lib, rows=(0, 0), ldy=1) == SHAPE            # N = 0
+    assert gs_(lib, rows=(1 << 30, 1 << 30), ldy=1 << 31) == SHAPE   # N > INT_MAX
+    assert gs_(lib, ldy=11) == SHAPE                        # ldy < N = 12
+    assert gs_(lib, od=2) == DTYPE
+    assert gs_(lib, K=24) == SHAPE
+    assert gs_(lib, mgs=None) == NULL
+    for i in range(5):
+        p = [P16] * 5
+        p[i] = None
+        assert gs_(lib, ptrs=p) == NULL
+    assert gs_(lib, mgs=ctypes.c_void_p(0x10002)) == ALIGN
+    assert gs_(lib, M=0, y=None, ptrs=[None] * 5, mgs=None) == OK
+    assert lib.nvfp4_last_hip_error() == 0
+
+
 def h(lib, scales=P16, mgs=P16, rows=(8, 4), K=32, sgs=ctypes.c_void_p(0x20000), counters=None):
     arr = (ctypes.c_int64 * len(rows))(*rows)
     return lib.nvfp4_harmonize_fused_scales(scales, mgs, arr, len(rows), K, sgs, counters, None)

@@ -1,6 +1,7 @@
 """Fused-projection harmonization on the GPU against the oracle, and the
-three-way comparison of the fused GDN in-projection: naive fused (one
-module's scale for every column), harmonized fused, and per-module."""
+comparison of the fused GDN in-projection: naive fused (one module's scale
+for every column), harmonized fused, segmented epilogue (each module's scale
+on its columns) and per-module."""
 import numpy as np
 import pytest
 import torch
@@ -54,8 +55,9 @@ def test_harmonize_power_of_two_ratios_exact():
     assert np.array_equal(got, want)
 
 
-def test_fused_gdn_three_way():
-    """C4: naive fused vs harmonized fused vs per-module, on sampled rows of X."""
+def test_fused_gdn_fused_variants():
+    """C4: naive fused, harmonized fused and segmented epilogue against their
+    oracles, and harmonized against per-module, on sampled rows of X."""
     need_gpu()
     cfg = CONFIGS["fused_gdn"]
     kind, rows, cols, dtype = cfg["x"]
@@ -75,6 +77,7 @@ def test_fused_gdn_three_way():
         ws_dev = gpu_u8(ws)
         shared, _ = nv.harmonize_fused_scales(ws_dev, gs_dev, [q[0].shape[0] for _, q in mods], cols)
         harm = nv.gemm(ac, as_, ga, gpu_u8(wc), ws_dev, shared)
+        seg = nv.gemm_segmented(ac, as_, ga, gpu_u8(wc), gpu_u8(ws), gs_dev, [q[0].shape[0] for _, q in mods])
         torch.cuda.synchronize()
 
         rng = np.random.default_rng(0)
@@ -82,6 +85,8 @@ def test_fused_gdn_three_way():
         a_s = (oa[0][sel], oa[1][sel], oa[2])
         Yn, Sn = ref.naive_fused_ref(*a_s, wc, ws, gs)
         assert_gemm_close(naive[sel], Yn, Sn, "naive fused")
+        Ys, Ss = ref.gemm_segmented_ref(*a_s, wc, ws, gs, [q[0].shape[0] for _, q in mods])
+        assert_gemm_close(seg[sel], Ys, Ss, "segmented epilogue")
         hs, hg, _, _ = ref.harmonize_ref([q[1] for _, q in mods], gs)
         Yh, Sh = ref.gemm_ref(*a_s, wc, hs, hg)
         assert_gemm_close(harm[sel], Yh, Sh, "harmonized fused")

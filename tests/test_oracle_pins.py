@@ -399,3 +399,58 @@ def test_naive_fused_closed_form():
         blk = y_naive[:, row:row + c.shape[0]]
         assert np.allclose(blk, y_i * (np.float64(gs[0]) / np.float64(g)), rtol=1e-12, atol=0)
         row += c.shape[0]
+
+
+# ------------------------------------------------------- segmented epilogue
+def test_segmented_gemm_column_loop_with_ragged_and_empty_modules():
+    """Each output column carries the tensor scale of the module its weight row
+    came from, found here by repeating module indices (not by slicing): a wrong
+    range boundary, an empty module or a dropped g_i fails."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_t(3, (3, 64)).astype(np.float32)
+    ac, as_, ga = _quant(x)
+    rows = [3, 0, 5, 1]
+    mults = [1.0, 7.0, 0.1, 40.0]
+    parts = [_quant((rng.standard_normal((r, 64)) * 0.02 * m).astype(np.float32)) for r, m in zip(rows, mults)]
+    wc = np.concatenate([p[0] for p in parts])
+    ws = np.concatenate([p[1] for p in parts])
+    gs = [p[2] for p in parts]
+    y, sabs = ref.gemm_segmented_ref(ac, as_, ga, wc, ws, gs, rows)
+    owner = np.repeat(np.arange(len(rows)), rows)
+    A = ref.dequantize(ac, as_, 1.0, include_global=False)
+    W = ref.dequantize(wc, ws, 1.0, include_global=False)
+    assert y.shape == (3, sum(rows))
+    for n in range(sum(rows)):
+        g = np.float64(ga) * np.float64(gs[owner[n]])
+        for m in range(3):
+            terms = A[m] * W[n] * g
+            assert abs(y[m, n] - terms.sum()) <= 1e-12 * np.abs(terms).sum()
+            assert abs(sabs[m, n] - np.abs(terms).sum()) <= 1e-12 * np.abs(terms).sum()
+
+
+def test_segmented_gemm_special_cases():
+    """One module is the plain GEMM; modules sharing one scale are the plain
+    GEMM of their concatenation; power-of-two ratios make the harmonized GEMM
+    equal to the segmented one."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_t(3, (4, 128)).astype(np.float32)
+    ac, as_, ga = _quant(x)
+    mods = _modules(6)
+    wc = np.concatenate([m[0] for m in mods])
+    ws = np.concatenate([m[1] for m in mods])
+    rows = [m[0].shape[0] for m in mods]
+    g = mods[0][2]
+    y1, s1 = ref.gemm_segmented_ref(ac, as_, ga, wc, ws, [g], [sum(rows)])
+    y0, s0 = ref.gemm_ref(ac, as_, ga, wc, ws, g)
+    assert np.array_equal(y1, y0) and np.array_equal(s1, s0)
+    y2, _ = ref.gemm_segmented_ref(ac, as_, ga, wc, ws, [g] * 4, rows)
+    assert np.allclose(y2, y0, rtol=1e-13, atol=1e-300)
+    gs = [g, np.float32(g / 2), np.float32(g / 8), np.float32(g * 2)]
+    # re-quantize each module with its own power-of-two-related scale
+    parts = [_quant((rng.standard_normal((r, 128)) * 0.02).astype(np.float32), g=gi) for r, gi in zip(rows, gs)]
+    wc = np.concatenate([p[0] for p in parts])
+    hs, g_star, n_inexact, n_sub = ref.harmonize_ref([p[1] for p in parts], gs)
+    assert n_inexact == 0 and n_sub == 0
+    y_seg, s_seg = ref.gemm_segmented_ref(ac, as_, ga, wc, np.concatenate([p[1] for p in parts]), gs, rows)
+    y_har, _ = ref.gemm_ref(ac, as_, ga, wc, hs, g_star)
+    assert np.all(np.abs(y_seg - y_har) <= 1e-13 * s_seg)
