@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--tokens", type=int, default=TOKENS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the segmented-epilogue and decode measurements (for counter runs)")
     ap.add_argument("--cpu-rows", type=int, default=6144, help="token rows in the CPU oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration) and exit")
@@ -116,6 +118,7 @@ def main():
     in_codes = torch.cat([wq[n][0] for n in fused])
     in_scales = torch.cat([wq[n][1] for n in fused])
     module_gs = torch.cat([wq[n][2] for n in fused])
+    in_scales_modules = in_scales.clone()   # per-module block scales, for the segmented epilogue
     in_gs, harm_counters = nv.harmonize_fused_scales(in_scales, module_gs, [P[n].n for n in fused], 5120)
     gemms = [  # (name, activation input index, codes, scales, gs, N, K)
         ("in_proj", 0, in_codes, in_scales, in_gs, in_codes.shape[0], 5120),
@@ -213,6 +216,9 @@ def main():
     except Exception:  # noqa: BLE001  (report, never fail the bench on this extra)
         amax_ms = None
 
+    extra = {} if args.no_extras else extra_measurements(nv, torch, np, dev, stream, xs, calib, qbuf, ys, in_codes,
+                                                         in_scales_modules, module_gs, [P[n].n for n in fused], T)
+
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -233,10 +239,71 @@ def main():
         "harmonize_counters": [int(v) for v in harm_counters.cpu().tolist()],
         "roofline": roofline,
         "roofline_quantize": roofline_q,
+        **extra,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows, xs, gemms, wq, fused, P, seed)
     print(json.dumps(out), flush=True)
+
+
+def extra_measurements(nv, torch, np, dev, stream, xs, calib, qbuf, ys, in_codes, in_scales_modules,
+                       module_gs, module_rows, T):
+    """Measurements next to the step (not part of `value`): the fused
+    in-projection with the segmented epilogue (per-module tensor scales)
+    instead of harmonized scales, and decode-sized GEMMs against the fused
+    in-projection weight (8 rotated copies, so the weight stream comes from
+    HBM, not the 256 MB last-level cache), timed with the launch queue
+    pre-filled so that the figure is GPU time, not host launch rate."""
+    out = {}
+    n, k = in_codes.shape[0], 5120
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nv.gemm_segmented(qbuf[0][0], qbuf[0][1], calib[0], in_codes, in_scales_modules, module_gs, module_rows,
+                      out_dtype=torch.bfloat16, out=ys[0])
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        nv.gemm_segmented(qbuf[0][0], qbuf[0][1], calib[0], in_codes, in_scales_modules, module_gs, module_rows,
+                          out_dtype=torch.bfloat16, out=ys[0])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    out["in_proj_segmented_epilogue"] = {"gemm_ms": round(ms, 4), "gemm_tflops": round(2.0 * T * n * k / ms / 1e9, 1)}
+
+    copies = [(in_codes.clone(), in_scales_modules.clone()) for _ in range(8)]
+    dec = {}
+    reps = 200
+    for m in (1, 8, 16, 32, 64):
+        x = xs[0][:m]
+        ac = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+        as_ = torch.empty((m, k // 16), dtype=torch.uint8, device=dev)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        nv.quantize(x, calib[0], from_amax=False, codes=ac, scales=as_)
+
+        def gemm_only(r):
+            nv.gemm_segmented(ac, as_, calib[0], copies[r % 8][0], copies[r % 8][1], module_gs, module_rows,
+                              out_dtype=torch.bfloat16, out=y)
+
+        def chain(r):
+            nv.quantize(x, calib[0], from_amax=False, codes=ac, scales=as_)
+            gemm_only(r)
+
+        res = {}
+        for label, fn in (("gemm_us", gemm_only), ("quantize_plus_gemm_us", chain)):
+            for r in range(16):
+                fn(r)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(50_000_000)   # keeps the GPU busy while the host enqueues
+            e0.record(stream)
+            for r in range(reps):
+                fn(r)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[label] = round(e0.elapsed_time(e1) / reps * 1e3, 2)
+        res["weight_gbps"] = round(n * k * 0.5625 / (res["gemm_us"] * 1e-6) / 1e9, 1)
+        dec[str(m)] = res
+    out["decode_in_proj_12384x5120"] = dec
+    del copies
+    return out
 
 
 def cpu_baseline(rows, xs, gemms, wq, fused, P, seed):

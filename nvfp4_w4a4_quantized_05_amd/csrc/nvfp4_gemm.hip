@@ -27,6 +27,7 @@
 //    always sit inside one 16-value block, i.e. one scale.
 //  * The RN32(g_a g_w) multiply and the fp32 or bf16 (RNE) conversion happen
 //    in the epilogue, straight from the accumulators.
+#include <cstdint>
 #include <type_traits>
 
 #include "nvfp4_device.h"
@@ -57,6 +58,16 @@ __device__ __forceinline__ half8_t dequant8(uint32_t codes, uint32_t s2) {
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
+}
+
+// Marks MFMA operands as still in use at this point of the program, so the
+// register allocator cannot hand their registers to a new value before it.
+template <int A, int B>
+__device__ __forceinline__ void keep_live(const half8_t (&x)[A], const half8_t (&y)[B]) {
+#pragma unroll
+  for (int i = 0; i < A; ++i) __asm__ volatile("" ::"v"(x[i]));
+#pragma unroll
+  for (int i = 0; i < B; ++i) __asm__ volatile("" ::"v"(y[i]));
 }
 
 // Tile order: workgroups go round-robin to the 8 XCDs, so consecutive ids
@@ -634,9 +645,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
 // Decode kernel (M <= 64, K % 256 == 0): bound by the weight stream,
 // N x K x 0.5625 bytes, which is read exactly once.
 //
-// A workgroup owns 48 weight rows (three 16-row MFMA blocks; N = 12288 gives
-// 256 workgroups, one per CU) and all M rows of A; its 4 waves split K into
-// quarters of nt tiles of 256 values.  Codes go straight into registers, D
+// A workgroup owns NB 16-row MFMA blocks of weight rows (the launcher picks
+// NB = 1..4 so that the workgroups fill the 256 CUs with the fewest rounds:
+// N = 12288 gives 256 workgroups of 48 rows) and all M rows of A; its 4
+// waves split K into quarters of nt tiles of 256 values.  Codes go straight into registers, D
 // tiles ahead; only the scale bytes and the final reduction use LDS.
 //
 //  * One code load reads 8 rows x 128 contiguous bytes (lane L: row L % 8,
@@ -654,19 +666,20 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
 //  * Rows >= M and rows >= N read zeros through the buffer bounds.
 //  * The four K-quarter partial sums are added through LDS in a fixed order
 //    (deterministic), then scaled by RN32(g_a g_w) and stored.
-// MB16 = number of 16-row blocks of A (1, 2 or 4); D = tiles in flight.
-template <int MB16>
-constexpr int decode_scale_rows() { return 48 + 16 * MB16; }
+// MB16 = number of 16-row blocks of A (1, 2 or 4); NB = number of 16-row
+// blocks of W; D = tiles in flight.
+template <int MB16, int NB>
+constexpr int decode_scale_rows() { return 16 * NB + 16 * MB16; }
 
-template <int MB16, int D, bool kOutBf16>
+template <int MB16, int NB, int D>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const ColScales cs,
-    int M, int N, int K, void* __restrict__ y, int64_t ldy, int nt_max) {
-  constexpr int NW = 48;  // weight rows per workgroup
+    int M, int N, int K, void* __restrict__ y, int64_t ldy, bool out_bf16, int nt_max) {
+  constexpr int NW = 16 * NB;  // weight rows per workgroup
   constexpr int MA = 16 * MB16;
   constexpr int kTileBytes = 128, kTileScales = 16;  // per row, per 256-value tile
-  constexpr int kLoads = 6 + 2 * MB16;               // code loads per tile
+  constexpr int kLoads = 2 * NB + 2 * MB16;          // code loads per tile
   static_assert(D * kLoads < 64, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) uint8_t dsmem[];
 
@@ -678,7 +691,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
   const int kt = K / 256;
   const int t0 = (kt * wave) / 4, nt = (kt * (wave + 1)) / 4 - t0;
   const int run = nt * kTileScales;  // scale bytes per row in this wave's range
-  uint8_t* const wsl = dsmem + wave * decode_scale_rows<MB16>() * nt_max * kTileScales;  // [48 rows][run]
+  uint8_t* const wsl = dsmem + wave * decode_scale_rows<MB16, NB>() * nt_max * kTileScales;  // [NW rows][run]
   uint8_t* const asl = wsl + NW * run;                                                  // [MA rows][run]
 
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_codes, (int64_t)N * row_bytes);
@@ -703,16 +716,16 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
   }
 
   // per-lane code offsets at tile 0 of this wave's K range
-  uint32_t w_off[6], a_off[2 * MB16];
+  uint32_t w_off[2 * NB], a_off[2 * MB16];
 #pragma unroll
-  for (int i = 0; i < 6; ++i)  // block i / 2, rows 8 (i % 2) .. + 7
+  for (int i = 0; i < 2 * NB; ++i)  // block i / 2, rows 8 (i % 2) .. + 7
     w_off[i] = (uint32_t)(n0 + 8 * i + (lane & 7)) * row_bytes + (uint32_t)(lane >> 3) * 16;
 #pragma unroll
   for (int i = 0; i < 2 * MB16; ++i)
     a_off[i] = (uint32_t)(8 * i + (lane & 7)) * row_bytes + (uint32_t)(lane >> 3) * 16;
 
   struct Tile {
-    u32x4_t w[6];
+    u32x4_t w[2 * NB];
     u32x4_t a[2 * MB16];
   };
   // Tile t0 + t of this wave.  Tiles past the wave's range (t >= nt) are
@@ -725,16 +738,16 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
     const bool ok = t < nt;
     const uint32_t kc = (uint32_t)(t0 + t) * kTileBytes;
 #pragma unroll
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < 2 * NB; ++i)
       T.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? w_off[i] + kc : kOutside, 0, 0);
 #pragma unroll
     for (int i = 0; i < 2 * MB16; ++i)
       T.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off[i] + kc : kOutside, 0, 0);
   };
 
-  floatx4_t acc[3][MB16];
+  floatx4_t acc[NB][MB16];
 #pragma unroll
-  for (int j = 0; j < 3; ++j)
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int b = 0; b < MB16; ++b)
 #pragma unroll
@@ -750,49 +763,61 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
     }
   };
 
+  // dequantized MFMA operands of the last three steps (see compute)
+  half8_t wv[3][NB], av[3][MB16];
   auto compute = [&](const Tile& T, int t) {
     // scale dword of the lane (4 blocks: chunks 2g and 2g + 1); phantom
     // tiles read the last real tile's scales (their codes are zero)
     const int ts = min(t, nt - 1) * kTileScales + 4 * g;
-    uint32_t wsd[3], asd[MB16];
+    uint32_t wsd[NB], asd[MB16];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) wsd[j] = *reinterpret_cast<const uint32_t*>(wsl + (16 * j + q) * run + ts);
+    for (int j = 0; j < NB; ++j) wsd[j] = *reinterpret_cast<const uint32_t*>(wsl + (16 * j + q) * run + ts);
 #pragma unroll
     for (int b = 0; b < MB16; ++b) asd[b] = *reinterpret_cast<const uint32_t*>(asl + (16 * b + q) * run + ts);
-    u32x4_t wr[3][2], ar[MB16][2];
+    u32x4_t wr[NB][2], ar[MB16][2];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) to_mfma_rows(T.w[2 * j], T.w[2 * j + 1], wr[j][0], wr[j][1]);
+    for (int j = 0; j < NB; ++j) to_mfma_rows(T.w[2 * j], T.w[2 * j + 1], wr[j][0], wr[j][1]);
 #pragma unroll
     for (int b = 0; b < MB16; ++b) to_mfma_rows(T.a[2 * b], T.a[2 * b + 1], ar[b][0], ar[b][1]);
     // step s: chunk s / 4, dword s % 4; its scale is byte 2 (s / 4) + (s % 4) / 2
-    // of the lane's scale dword.  Operands of step s + 1 are dequantized into
-    // the other half of a double buffer while the MFMAs of step s run: a VALU
-    // write to a 16x16x32 MFMA's source registers right behind its issue was
-    // seen to corrupt the MFMA's input.
-    half8_t wv[2][3], av[2][MB16];
+    // of the lane's scale dword.  Operands of step s + 1 are dequantized while
+    // the MFMAs of step s issue, and the operands of step s - 1 are kept live
+    // until the MFMAs of step s have issued (an empty asm that uses them).
+    // An earlier version of this kernel produced wrong rows 8-15 of its
+    // 16x16x32 MFMA blocks when a VALU wrote an MFMA's A/B registers right
+    // behind its issue; the register allocator reuses those registers at once
+    // unless they are still live, so the liveness is extended on purpose.
+    // The last step's operands are kept live by the caller, past the next
+    // refill.
     auto deq = [&](int s, int slot) {
       const int c = s >> 2, dw = s & 3, sb = 8 * (2 * c + (dw >> 1));
 #pragma unroll
       for (int b = 0; b < MB16; ++b) av[slot][b] = dequant8(ar[b][c][dw], scale_pair((asd[b] >> sb) & 0xFFu));
 #pragma unroll
-      for (int j = 0; j < 3; ++j) wv[slot][j] = dequant8(wr[j][c][dw], scale_pair((wsd[j] >> sb) & 0xFFu));
+      for (int j = 0; j < NB; ++j) wv[slot][j] = dequant8(wr[j][c][dw], scale_pair((wsd[j] >> sb) & 0xFFu));
     };
     deq(0, 0);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      if (s + 1 < 8) deq(s + 1, (s + 1) & 1);
+      if (s + 1 < 8) deq(s + 1, (s + 1) % 3);
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int b = 0; b < MB16; ++b)
-          acc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv[s & 1][j], av[s & 1][b], acc[j][b], 0, 0, 0);
+          acc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv[s % 3][j], av[s % 3][b], acc[j][b], 0, 0, 0);
       if (s + 1 < 8) {
+        constexpr int kMfma = NB * MB16, kValu = (8 * (NB + MB16) + kMfma - 1) / kMfma;
 #pragma unroll
-        for (int i = 0; i < 3 * MB16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                             // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, (8 * (3 + MB16) + 3 * MB16 - 1) / (3 * MB16), 0);  // VALU
+        for (int i = 0; i < kMfma; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
         }
       }
+      // step s - 1's operands stay live until every instruction of step s
+      // has issued (the barrier keeps the scheduler from moving MFMAs past
+      // the asm)
+      __builtin_amdgcn_sched_barrier(0);
+      if (s > 0) keep_live(wv[(s + 2) % 3], av[(s + 2) % 3]);
     }
   };
 
@@ -803,10 +828,13 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
       load(ring[u], u);
       __builtin_amdgcn_sched_barrier(0);  // issue the tiles in order
     }
-    // The scale copies were issued before the code loads and complete in
-    // order: once at most D * kLoads loads are outstanding they have landed.
-    wait_vmcnt<D * kLoads>();
-    __asm__ volatile("" ::: "memory");
+    // The scale copies to LDS must have landed before the first scale read.
+    // Waiting for every load in flight is the only count that holds however
+    // the compiler orders the code loads around this point (a count of
+    // D * kLoads is not: the compiler may issue part of the ring after the
+    // wait, and the copies were then still in flight on a cold start).
+    wait_vmcnt<0>();
+    __asm__ volatile("" ::: "memory");  // no LDS read moves above the wait
     const int n_full = nt / D;
     for (int it = 0; it < n_full; ++it) {
 #pragma unroll
@@ -817,36 +845,41 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
         __builtin_amdgcn_sched_barrier(0);
         load(ring[u], it * D + u + D);
         __builtin_amdgcn_sched_barrier(0);
+        keep_live(wv[7 % 3], av[7 % 3]);  // last step's operands, past the refill
       }
     }
     // the last nt % D tiles are already in the ring
 #pragma unroll
     for (int u = 0; u + 1 < D; ++u)
-      if (u < nt - n_full * D) compute(ring[u], n_full * D + u);
+      if (u < nt - n_full * D) {
+        compute(ring[u], n_full * D + u);
+        __builtin_amdgcn_sched_barrier(0);
+        keep_live(wv[7 % 3], av[7 % 3]);
+      }
   }
 
   // fixed-order sum of the 4 K quarters through LDS (the scale area is free
   // once every wave has passed the barrier)
   __syncthreads();
-  float* red = reinterpret_cast<float*>(dsmem);  // [3 waves][3][MB16][4][64]
+  float* red = reinterpret_cast<float*>(dsmem);  // [3 waves][NB][MB16][4][64]
   if (wave > 0) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int b = 0; b < MB16; ++b)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[(((wave - 1) * 3 + j) * MB16 + b) * 256 + v * 64 + lane] = acc[j][b][v];
+        for (int v = 0; v < 4; ++v) red[(((wave - 1) * NB + j) * MB16 + b) * 256 + v * 64 + lane] = acc[j][b][v];
   }
   __syncthreads();
   if (wave == 0) {
-    // one tensor scale for the workgroup's 48 columns unless a column range
+    // one tensor scale for the workgroup's columns unless a column range
     // ends inside them
     const float g_a = *a_gs;
     const int s_first = col_range(cs, n0), s_last = col_range(cs, min(n0 + NW, N) - 1);
     const float alpha_u = g_a * cs.gs[s_first];
     const bool vec_ok = (ldy % 4 == 0) && ((uintptr_t)y % 16 == 0);
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int b = 0; b < MB16; ++b) {
         const int m = 16 * b + q;
@@ -856,11 +889,11 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
         for (int v = 0; v < 4; ++v) {
           float t = acc[j][b][v];
 #pragma unroll
-          for (int w = 0; w < 3; ++w) t += red[((w * 3 + j) * MB16 + b) * 256 + v * 64 + lane];
+          for (int w = 0; w < 3; ++w) t += red[((w * NB + j) * MB16 + b) * 256 + v * 64 + lane];
           o[v] = t * (s_first == s_last ? alpha_u : col_alpha(g_a, cs, n + v));
         }
         if (m < M) {
-          if constexpr (kOutBf16) {
+          if (out_bf16) {
             __bf16* dst = reinterpret_cast<__bf16*>(y) + (int64_t)m * ldy + n;
             if (vec_ok && n + 3 < N) {
               typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -896,10 +929,10 @@ bool allow_lds(const void* fn, size_t bytes) {
 
 // LDS bytes of a decode launch: the per-wave scale runs, or the reduction
 // buffer if larger.
-template <int MB16>
+template <int MB16, int NB>
 size_t decode_lds_bytes(int nt_max) {
-  const size_t scales = (size_t)4 * decode_scale_rows<MB16>() * nt_max * 16;
-  const size_t red = (size_t)3 * 3 * MB16 * 4 * 64 * sizeof(float);
+  const size_t scales = (size_t)4 * decode_scale_rows<MB16, NB>() * nt_max * 16;
+  const size_t red = (size_t)3 * NB * MB16 * 4 * 64 * sizeof(float);
   return scales > red ? scales : red;
 }
 
@@ -952,27 +985,41 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   const bool fits_decode = (N + 64) * (K / 2) < ((int64_t)1 << 31) && M * (K / 2) < ((int64_t)1 << 31);
   if (aligned && fits_decode && M <= 64 && K % 256 == 0) {
     const int nt_max = (int)((K / 256 + 3) / 4);
-    const dim3 grid((unsigned)((N + 47) / 48)), block(256);
+    // NB 16-row weight blocks per workgroup: the fewest rounds of 256
+    // workgroups times the blocks each one streams (ties: more blocks, so
+    // fewer workgroups re-read A)
+    const int64_t rb = (N + 15) / 16;
+    int nb = 4;
+    int64_t best = INT64_MAX;
+    for (int c = 4; c >= 1; --c) {
+      const int64_t cost = ((rb + c - 1) / c + 255) / 256 * c;
+      if (cost < best) { best = cost; nb = c; }
+    }
+    const dim3 grid((unsigned)((rb + nb - 1) / nb)), block(256);
     const int m = (int)M, n = (int)N, k = (int)K;
-#define NVFP4_DECODE(MB, DD)                                                                                   \
+#define NVFP4_DECODE_NB(MB, NBB, DD)                                                                           \
   do {                                                                                                          \
-    const size_t lds = decode_lds_bytes<MB>(nt_max);                                                            \
-    const void* fn = out_bf16 ? (const void*)gemm_decode_kernel<MB, DD, true>                                   \
-                              : (const void*)gemm_decode_kernel<MB, DD, false>;                                 \
-    if (lds <= kDecodeMaxLds && allow_lds(fn, lds)) {                                                           \
-      if (out_bf16)                                                                                             \
-        gemm_decode_kernel<MB, DD, true><<<grid, block, lds, stream>>>(a_codes, a_scales, a_gs, w_codes,        \
-                                                                       w_scales, cs, m, n, k, y, ldy, nt_max); \
-      else                                                                                                      \
-        gemm_decode_kernel<MB, DD, false><<<grid, block, lds, stream>>>(a_codes, a_scales, a_gs, w_codes,       \
-                                                                        w_scales, cs, m, n, k, y, ldy, nt_max); \
+    const size_t lds = decode_lds_bytes<MB, NBB>(nt_max);                                                       \
+    if (lds <= kDecodeMaxLds && allow_lds((const void*)gemm_decode_kernel<MB, NBB, DD>, lds)) {                \
+      gemm_decode_kernel<MB, NBB, DD><<<grid, block, lds, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, \
+                                                                    cs, m, n, k, y, ldy, out_bf16, nt_max);     \
       return hipGetLastError();                                                                                 \
     }                                                                                                           \
+  } while (0)
+#define NVFP4_DECODE(MB, DD)                  \
+  do {                                        \
+    switch (nb) {                             \
+      case 1: NVFP4_DECODE_NB(MB, 1, DD); break; \
+      case 2: NVFP4_DECODE_NB(MB, 2, DD); break; \
+      case 3: NVFP4_DECODE_NB(MB, 3, DD); break; \
+      default: NVFP4_DECODE_NB(MB, 4, DD); break; \
+    }                                         \
   } while (0)
     if (M <= 16) NVFP4_DECODE(1, 3);
     else if (M <= 32) NVFP4_DECODE(2, 3);
     else NVFP4_DECODE(4, 2);
 #undef NVFP4_DECODE
+#undef NVFP4_DECODE_NB
   }
   return launch_tiles<128, 128, 64, 64>(a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y,
                                         out_bf16, ldy, aligned, stream);

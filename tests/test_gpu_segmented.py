@@ -28,11 +28,14 @@ def _case(M, rows, K, seed, mults):
     return aq, wc, ws, gs
 
 
-# (M, module rows, K): decode kernel (M <= 64, K % 256 == 0), generic kernel
-# (K % 128 != 0), streaming kernel (>= 256 tiles of 256 x 256); boundaries
-# fall inside 16-, 128- and 256-column tiles, one module is empty.
+# (M, module rows, K): decode kernel (M <= 64, K % 256 == 0; workgroups of
+# 16, 32 and 64 weight rows), generic kernel (K % 128 != 0), streaming kernel
+# (>= 256 tiles of 256 x 256); boundaries fall inside workgroup tiles, one
+# module is empty.
 SHAPES = [
     (5, (40, 0, 17, 7), 512),
+    (3, (8192, 4096, 48, 48), 512),
+    (20, (2000, 3000, 120), 256),
     (64, (8192 // 64, 48, 48, 300), 1024),
     (37, (100, 3, 60), 144),
     (300, (130, 0, 77, 49), 384),
