@@ -492,65 +492,114 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
-  auto mfma_step = [&](int cur) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[cur][j], af[cur][i], acc[j][i], 0, 0, 0);
-  };
-  // Issue order inside one MFMA step: each MFMA is followed by 4 VALU
-  // (dequantization of the next step) and optionally one copy and/or LDS read.
-  auto schedule = [&](int n_vmem, int n_ds) {
-#pragma unroll
-    for (int g = 0; g < FM * FN; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);    // VALU
-      if (g < n_vmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (copy)
-      if (g < n_ds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
+  // Main loop: a fixed software pipeline.  Each of the 8 MFMA steps of a K
+  // tile issues its 16 MFMAs one at a time, each followed by one chunk of
+  // the dequantization of the next step (about 4-7 VALU) and, in some steps,
+  // one LDS read or one copy; a scheduling barrier after every group keeps
+  // that order, so the dequantization runs in the shadow of the matrix
+  // instructions instead of in blocks between them.  Step 7 dequantizes
+  // step 0 of the next K tile (its half 0 and scales are read at mid-tile).
+  //
+  // Operand chunks follow the order in which the previous step last read
+  // the operand's registers (W block j is last read by MFMA 4j + 3, A block
+  // i by MFMA 12 + i): W0, W1, A0, A1, A2, A3, W2, W3.
+  half2_t part[2];  // first half of an operand, between its two chunks
+  auto dequant_chunk = [&](int t, int slot, int c, bool next_tile) {
+    const int op = c >> 1, second = c & 1;
+    constexpr int kOrder[8] = {4, 5, 0, 1, 2, 3, 6, 7};  // 0..3: A blocks, 4..7: W blocks
+    const int o = kOrder[op];
+    const bool is_w = o >= 4;
+    const int idx = is_w ? o - 4 : o;
+    const uint32_t sc = is_w ? (next_tile ? w_sc_next[idx] : w_sc[idx]) : (next_tile ? a_sc_next[idx] : a_sc[idx]);
+    const uint32_t codes = is_w ? w_raw[idx][t >> 2][t & 3] : a_raw[idx][t >> 2][t & 3];
+    const half2_t sp = __builtin_bit_cast(half2_t, scale_pair((sc >> (8 * (t >> 1))) & 0xFFu));
+    if (!second) {
+      part[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * sp;
+      part[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * sp;
+    } else {
+      const half2_t q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * sp;
+      const half2_t q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * sp;
+      half8_t r;
+      r[0] = part[0][0]; r[1] = part[0][1]; r[2] = part[1][0]; r[3] = part[1][1];
+      r[4] = q0[0]; r[5] = q0[1]; r[6] = q1[0]; r[7] = q1[1];
+      if (is_w) wf[slot][idx] = r;
+      else af[slot][idx] = r;
     }
   };
 
-  // first K tile: wait for its copies, then read its first half + scales
+  // first K tile: wait for its copies, read its first half + scales and
+  // dequantize its step 0
   wait_vmcnt<(STAGES - 1) * kLoadsPerStage>();
   __builtin_amdgcn_s_barrier();
   read_half(0, 0, true);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) a_sc[i] = a_sc_next[i];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) w_sc[j] = w_sc_next[j];
+  dequant_step(0, 0);
+
+  // LDS reads of half h of a stage, one per call (g = 0..FM+FN-1 codes,
+  // then FM+FN scale dwords when with_scales)
+  auto read_one = [&](int slot, int h, int g) {
+    const uint8_t* st = ring + slot * kStageBytes;
+    if (g < FM) {
+      const int row = wave_m * WM + g * 32 + r32;
+      a_raw[g][h] = *reinterpret_cast<const u32x4_t*>(st + row * kRowBytes + 16 * ((2 * half + h) ^ chunk_swizzle(row)));
+    } else if (g < FM + FN) {
+      const int row = wave_n * WN + (g - FM) * 32 + r32;
+      w_raw[g - FM][h] = *reinterpret_cast<const u32x4_t*>(st + kCodeBytes + row * kRowBytes + 16 * ((2 * half + h) ^ chunk_swizzle(row)));
+    } else if (g < 2 * FM + FN) {
+      const int row = wave_m * WM + (g - FM - FN) * 32 + r32;
+      a_sc_next[g - FM - FN] = *reinterpret_cast<const uint32_t*>(st + 2 * kCodeBytes + row * kScaleBytes + half * 4);
+    } else {
+      const int row = wave_n * WN + (g - 2 * FM - FN) * 32 + r32;
+      w_sc_next[g - 2 * FM - FN] =
+          *reinterpret_cast<const uint32_t*>(st + 2 * kCodeBytes + kStageScaleBytes + row * kScaleBytes + half * 4);
+    }
+  };
+  // the 12 copies of one stage, one per call
+  auto issue_one = [&](int ks, int slot, int g) {
+    uint8_t* st = ring + slot * kStageBytes;
+    const uint32_t kc = (uint32_t)ks * kRowBytes, kscl = (uint32_t)ks * kScaleBytes;
+    if (g < 4) lds_copy16(ra, a_off[g], kc, st + (wave * 64 + 16 * g) * kRowBytes);
+    else if (g < 8) lds_copy16(rw, w_off[g - 4], kc, st + kCodeBytes + (wave * 64 + 16 * (g - 4)) * kRowBytes);
+    else if (g < 10) lds_copy4(ras, as_off[g - 8], kscl, st + 2 * kCodeBytes + (wave * 64 + 32 * (g - 8)) * kScaleBytes);
+    else lds_copy4(rws, ws_off[g - 10], kscl, st + 2 * kCodeBytes + kStageScaleBytes + (wave * 64 + 32 * (g - 10)) * kScaleBytes);
+  };
 
   for (int ks = 0; ks < ksteps; ++ks) {
-    const int slot = ks % STAGES;
+    const int slot = ks % STAGES, next_slot = (ks + 1) % STAGES;
+    const int refill = min(ks + STAGES, ksteps - 1);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) a_sc[i] = a_sc_next[i];
+    for (int kk = 0; kk < 8; ++kk) {
+      const int cur = kk & 1;
+      if (kk == 4) {
+        // mid-tile: K tile ks+1 has landed (own copies + barrier), and every
+        // wave is done reading this slot (its half 1 was read in step 0), so
+        // the slot is refilled with K tile ks+STAGES (clamped).  A bare
+        // s_barrier: __syncthreads() would also wait for every copy in
+        // flight and drain the ring.
+        wait_vmcnt<(STAGES - 2) * kLoadsPerStage>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) w_sc[j] = w_sc_next[j];
-    // phase 1: MFMA steps 0..3 from half 0 while half 1 of this K tile is read
-    dequant_step(0, 0);
-    read_half(slot, 1, false);
-    dequant_step(1, 1);
-    mfma_step(0);
-    schedule(0, FM + FN);
+      for (int g = 0; g < FM * FN; ++g) {
+        const int j = g >> 2, i = g & 3;
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[cur][j], af[cur][i], acc[j][i], 0, 0, 0);
+        if (kk < 7) dequant_chunk(kk + 1, cur ^ 1, g, false);
+        else dequant_chunk(0, 0, g, true);  // step 0 of the next K tile
+        if (kk == 0 && g < FM + FN) read_one(slot, 1, g);  // half 1 of this K tile
+        if (kk == 4 && g < kLoadsPerStage) issue_one(refill, slot, g);
+        if (kk == 5) read_one(next_slot, 0, g);          // half 0 + scales of the next K tile
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (kk == 7) {
 #pragma unroll
-    for (int kk = 1; kk < 4; ++kk) {
-      dequant_step(kk + 1, (kk + 1) & 1);
-      mfma_step(kk & 1);
-      schedule(0, 0);
-    }
-    // mid-tile: K tile ks+1 has landed (own copies + barrier); the slot just
-    // read is refilled with K tile ks+STAGES (clamped)
-    wait_vmcnt<(STAGES - 2) * kLoadsPerStage>();
-    // a bare s_barrier: __syncthreads() would also wait for every copy in
-    // flight and drain the ring
-    __builtin_amdgcn_s_barrier();
-    issue_stage(min(ks + STAGES, ksteps - 1), slot);
-    read_half((ks + 1) % STAGES, 0, true);
-    // phase 2: MFMA steps 4..7 from half 1 while the next K tile's half 0 is read
-    dequant_step(5, 1);
-    mfma_step(0);
-    schedule(kLoadsPerStage, FM * FN);
+        for (int i = 0; i < FM; ++i) a_sc[i] = a_sc_next[i];
 #pragma unroll
-    for (int kk = 5; kk < 8; ++kk) {
-      if (kk + 1 < 8) dequant_step(kk + 1, (kk + 1) & 1);
-      mfma_step(kk & 1);
-      if (kk + 1 < 8) schedule(0, 0);
+        for (int j = 0; j < FN; ++j) w_sc[j] = w_sc_next[j];
+      }
     }
   }
   wait_vmcnt<0>();  // the repeated copies past the last K tile
