@@ -217,7 +217,8 @@ def main():
         amax_ms = None
 
     extra = {} if args.no_extras else extra_measurements(nv, torch, np, dev, stream, xs, calib, qbuf, ys, in_codes,
-                                                         in_scales_modules, module_gs, [P[n].n for n in fused], T)
+                                                         in_scales, in_gs, in_scales_modules, module_gs,
+                                                         [P[n].n for n in fused], T)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -246,14 +247,15 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def extra_measurements(nv, torch, np, dev, stream, xs, calib, qbuf, ys, in_codes, in_scales_modules,
+def extra_measurements(nv, torch, np, dev, stream, xs, calib, qbuf, ys, in_codes, in_scales, in_gs, in_scales_modules,
                        module_gs, module_rows, T):
     """Measurements next to the step (not part of `value`): the fused
     in-projection with the segmented epilogue (per-module tensor scales)
-    instead of harmonized scales, and decode-sized GEMMs against the fused
+    instead of harmonized scales, decode-sized GEMMs against the fused
     in-projection weight (8 rotated copies, so the weight stream comes from
-    HBM, not the 256 MB last-level cache), timed with the launch queue
-    pre-filled so that the figure is GPU time, not host launch rate."""
+    HBM, not the 256 MB last-level cache), and decode-sized quantize + GEMM
+    as one call against two launches, timed with the launch queue pre-filled
+    so that the figure is GPU time, not host launch rate."""
     out = {}
     n, k = in_codes.shape[0], 5120
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -302,7 +304,43 @@ def extra_measurements(nv, torch, np, dev, stream, xs, calib, qbuf, ys, in_codes
         res["weight_gbps"] = round(n * k * 0.5625 / (res["gemm_us"] * 1e-6) / 1e9, 1)
         dec[str(m)] = res
     out["decode_in_proj_12384x5120"] = dec
-    del copies
+
+    # quantize + GEMM as one call (nvfp4_quantize_gemm: one kernel for M <= 2,
+    # the workspace path above that) against the two launches, on the
+    # harmonized in-projection (one tensor scale), same queue discipline
+    hcopies = [(in_codes.clone(), in_scales.clone()) for _ in range(8)]
+    qg = {}
+    for m in (1, 2, 4):
+        x = xs[0][:m]
+        ac = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+        as_ = torch.empty((m, k // 16), dtype=torch.uint8, device=dev)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(1, nv.load().nvfp4_quantize_gemm_workspace_size(m, n, k, 1, 1)), dtype=torch.uint8,
+                         device=dev)
+
+        def two_launches(r):
+            nv.quantize(x, calib[0], from_amax=False, codes=ac, scales=as_)
+            nv.gemm(ac, as_, calib[0], hcopies[r % 8][0], hcopies[r % 8][1], in_gs, out_dtype=torch.bfloat16, out=y)
+
+        def one_call(r):
+            nv.quantize_gemm(x, calib[0], hcopies[r % 8][0], hcopies[r % 8][1], in_gs, out_dtype=torch.bfloat16,
+                             out=y, workspace=ws)
+
+        res = {"one_kernel": nv.load().nvfp4_quantize_gemm_workspace_size(m, n, k, 1, 1) == 0}
+        for label, fn in (("two_launches_us", two_launches), ("one_call_us", one_call)):
+            for r in range(16):
+                fn(r)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(50_000_000)
+            e0.record(stream)
+            for r in range(reps):
+                fn(r)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[label] = round(e0.elapsed_time(e1) / reps * 1e3, 2)
+        qg[str(m)] = res
+    out["decode_quantize_gemm_in_proj_12384x5120"] = qg
+    del copies, hcopies
     return out
 
 

@@ -158,6 +158,45 @@ NVFP4_API nvfp4_status_t nvfp4_gemm_segmented(const uint8_t* a_codes, const uint
                                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nvfp4_quantize_gemm -- quantize the activations with a given (calibrated)
+ * tensor scale and multiply: y = nvfp4_gemm(nvfp4_quantize(x, a_gs), W), in
+ * one call.  The activation quantization and the linear layer are the ones
+ * of nvfp4_quantize (GIVEN mode) and nvfp4_gemm (picx.dev summary,
+ * "Background", item 1); the pages' recipe calibrates the activation scales
+ * offline (LIT-800, "Key takeaways", recipe bullet), which is what makes the
+ * scale a given input here.
+ *
+ * For decode-sized bf16 inputs (1 <= M <= 2, K % 256 == 0, K <= 8192, and
+ * N, K small enough that nvfp4_quantize_gemm_workspace_size() returns 0)
+ * one kernel does both: every workgroup quantizes the activations of its K
+ * range into LDS while its weight loads are in flight, which saves the
+ * quantize launch of a decode step.  Other shapes quantize into the
+ * caller's workspace, then run the GEMM.  Either way the output is
+ * bit-identical to nvfp4_quantize followed by nvfp4_gemm.
+ *
+ *   x                 device, M x K activations, bf16 (NVFP4_IN_BF16) or fp32
+ *                     (NVFP4_IN_F32), row stride ldx >= K elements; 16-byte
+ *                     aligned rows (ldx * element size % 16 == 0)
+ *   a_gs              device, one float: the activations' tensor scale (read)
+ *   w_codes, w_scales, w_gs, N, K, y, out_dtype, ldy   as for nvfp4_gemm;
+ *                     the one-kernel path needs w_codes 16-byte and w_scales
+ *                     8-byte aligned (else NVFP4_ERR_ALIGN)
+ *   workspace         device scratch of nvfp4_quantize_gemm_workspace_size()
+ *                     bytes (16-byte aligned; may be NULL when that is 0)
+ * Errors as for nvfp4_quantize and nvfp4_gemm; NVFP4_ERR_WORKSPACE if the
+ * workspace is too small.
+ */
+NVFP4_API nvfp4_status_t nvfp4_quantize_gemm(const void* x, int32_t in_dtype, int64_t ldx, const float* a_gs,
+                                             const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
+                                             int64_t M, int64_t N, int64_t K, void* y, int32_t out_dtype,
+                                             int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace nvfp4_quantize_gemm needs: 0 when one kernel does both
+ * steps, else M*K/2 rounded up to 256 plus M*K/16 (codes, then scales). */
+NVFP4_API size_t nvfp4_quantize_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t in_dtype,
+                                                    int32_t out_dtype);
+
+/*
  * nvfp4_harmonize_fused_scales -- re-express the block scales of modules
  * that are concatenated along N into one fused weight, each quantized with
  * its own tensor scale g_i, under one shared tensor scale g* = max_i g_i

@@ -12,4 +12,5 @@ from ._lib import (  # noqa: F401
     harmonize_fused_scales,
     load,
     quantize,
+    quantize_gemm,
 )

@@ -22,7 +22,8 @@ SCALE_GIVEN, SCALE_FROM_AMAX = 0, 1
 STATUS_NAMES = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_DTYPE",
                 4: "NVFP4_ERR_MODE", 5: "NVFP4_ERR_ALIGN", 6: "NVFP4_ERR_WORKSPACE",
                 7: "NVFP4_ERR_HIP", 8: "NVFP4_ERR_ALIAS"}
-EXPORTS = ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_segmented", "nvfp4_harmonize_fused_scales",
+EXPORTS = ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_segmented", "nvfp4_quantize_gemm",
+           "nvfp4_quantize_gemm_workspace_size", "nvfp4_harmonize_fused_scales",
            "nvfp4_gemm_workspace_size", "nvfp4_status_string", "nvfp4_last_hip_error")
 
 _lib = None
@@ -54,6 +55,10 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_gemm_segmented.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(i64), i32, i64, i64, vp, i32,
                                          i64, vp, sz, vp]
     lib.nvfp4_gemm_segmented.restype = i32
+    lib.nvfp4_quantize_gemm.argtypes = [vp, i32, i64, vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp, sz, vp]
+    lib.nvfp4_quantize_gemm.restype = i32
+    lib.nvfp4_quantize_gemm_workspace_size.argtypes = [i64, i64, i64, i32, i32]
+    lib.nvfp4_quantize_gemm_workspace_size.restype = sz
     lib.nvfp4_harmonize_fused_scales.argtypes = [vp, vp, ctypes.POINTER(i64), i32, i64, vp, vp, vp]
     lib.nvfp4_harmonize_fused_scales.restype = i32
     lib.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64, i32]
@@ -176,6 +181,37 @@ def gemm_segmented(a_codes, a_scales, a_gs, w_codes, w_scales, module_gs, module
                                   _ptr(module_gs.contiguous()), host_rows, len(rows), M, K, _ptr(out), od,
                                   out.stride(0), _ptr(ws), ws_bytes, _stream(stream))
     _check(st, "nvfp4_gemm_segmented")
+    return out
+
+
+def quantize_gemm(x: torch.Tensor, a_gs: torch.Tensor, w_codes, w_scales, w_gs, *, out_dtype=torch.float32,
+                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """y = gemm(quantize(x, a_gs), W) in one call (one kernel for decode-sized x)."""
+    _need_gpu(x, a_gs, w_codes, w_scales, w_gs, out, workspace)
+    if x.dim() != 2 or x.stride(1) != 1 or x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be a 2-D bf16 or fp32 tensor with unit column stride")
+    M, K = x.shape
+    N = w_codes.shape[0]
+    if w_codes.shape[1] * 2 != K or w_scales.shape != (N, K // 16):
+        raise ValueError("operand shapes disagree")
+    for t in (w_codes, w_scales):
+        if not t.is_contiguous() or t.dtype != torch.uint8:
+            raise ValueError("codes and scales must be contiguous uint8")
+    dt = IN_BF16 if x.dtype == torch.bfloat16 else IN_F32
+    od = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[out_dtype]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    if out.dtype != out_dtype or out.stride(1) != 1:
+        raise ValueError("out must have unit column stride and dtype out_dtype")
+    lib = load()
+    ws_bytes = lib.nvfp4_quantize_gemm_workspace_size(M, N, K, dt, od)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    ws_ptr = _ptr(workspace) if ws_bytes else None
+    ws_have = workspace.numel() * workspace.element_size() if (ws_bytes and workspace is not None) else 0
+    st = lib.nvfp4_quantize_gemm(_ptr(x), dt, x.stride(0), _ptr(a_gs), _ptr(w_codes), _ptr(w_scales), _ptr(w_gs),
+                                 M, N, K, _ptr(out), od, out.stride(0), ws_ptr, ws_have, _stream(stream))
+    _check(st, "nvfp4_quantize_gemm")
     return out
 
 

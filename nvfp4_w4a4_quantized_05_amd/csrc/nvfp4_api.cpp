@@ -112,6 +112,60 @@ nvfp4_status_t nvfp4_gemm_segmented(const uint8_t* a_codes, const uint8_t* a_sca
   }
 }
 
+size_t nvfp4_quantize_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t in_dtype, int32_t out_dtype) {
+  (void)out_dtype;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0 || M > INT_MAX || K > INT_MAX) return 0;
+  if (nvfp4::quantize_gemm_fused_fits(M, N, K, in_dtype == NVFP4_IN_BF16)) return 0;
+  const int64_t code_bytes = (M * (K / 2) + 255) / 256 * 256;  // scales start 256-byte aligned
+  return (size_t)(code_bytes + M * (K / 16));
+}
+
+nvfp4_status_t nvfp4_quantize_gemm(const void* x, int32_t in_dtype, int64_t ldx, const float* a_gs,
+                                   const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
+                                   int64_t M, int64_t N, int64_t K, void* y, int32_t out_dtype, int64_t ldy,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (in_dtype != NVFP4_IN_F32 && in_dtype != NVFP4_IN_BF16) return NVFP4_ERR_DTYPE;
+    if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_DTYPE;
+    if (M < 0 || N <= 0 || K <= 0 || K % 16 != 0 || ldx < K || ldy < N) return NVFP4_ERR_SHAPE;
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX || M > INT64_MAX / ldx / 4) return NVFP4_ERR_SHAPE;
+    if (M == 0) return NVFP4_OK;
+    if (!x || !a_gs || !w_codes || !w_scales || !w_gs || !y) return NVFP4_ERR_NULL;
+    const int64_t esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
+    if (!aligned(x, 16) || (ldx * esize) % 16 != 0 || !aligned(a_gs, 4) || !aligned(w_gs, 4) ||
+        !aligned(y, out_dtype == NVFP4_OUT_BF16 ? 2 : 4))
+      return NVFP4_ERR_ALIGN;
+    const size_t need = nvfp4_quantize_gemm_workspace_size(M, N, K, in_dtype, out_dtype);
+    if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (need > 0 && !workspace) return NVFP4_ERR_NULL;
+    if ((M * (K / 16) + 255) / 256 > (int64_t)INT_MAX) return NVFP4_ERR_SHAPE;
+    nvfp4::ColScales cs{};
+    cs.gs = w_gs;
+    cs.n = 1;
+    cs.end[0] = (int)N;
+    const bool in_bf16 = in_dtype == NVFP4_IN_BF16, out_bf16 = out_dtype == NVFP4_OUT_BF16;
+    if (need == 0) {  // one kernel: the decode GEMM quantizes the activations itself
+      if (!aligned(w_codes, 16) || !aligned(w_scales, 8)) return NVFP4_ERR_ALIGN;
+      return hip_status(nvfp4::launch_quantize_gemm_fused(x, in_bf16, ldx, a_gs, w_codes, w_scales, cs, M, N, K,
+                                                          y, out_bf16, ldy, (hipStream_t)stream));
+    }
+    // two kernels through the workspace: quantize (given scale), then GEMM
+    if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
+    uint8_t* codes = static_cast<uint8_t*>(workspace);
+    uint8_t* scales = codes + (M * (K / 2) + 255) / 256 * 256;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles > (int64_t)INT_MAX) return NVFP4_ERR_SHAPE;
+    const nvfp4_status_t st = hip_status(nvfp4::launch_quantize(x, in_bf16, M, K, ldx, codes, scales,
+                                                                const_cast<float*>(a_gs), false,
+                                                                (hipStream_t)stream));
+    if (st != NVFP4_OK) return st;
+    return hip_status(nvfp4::launch_gemm(codes, scales, a_gs, w_codes, w_scales, cs, M, N, K, y, out_bf16, ldy,
+                                         (hipStream_t)stream));
+  } catch (...) {
+    return NVFP4_ERR_HIP;
+  }
+}
+
 nvfp4_status_t nvfp4_harmonize_fused_scales(uint8_t* scales, const float* module_gs,
                                             const int64_t* module_rows, int32_t n_modules,
                                             int64_t K, float* shared_gs, uint32_t* counters,

@@ -32,6 +32,7 @@
 
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
+#include "nvfp4_quant_block.h"
 
 namespace nvfp4 {
 namespace {
@@ -41,6 +42,12 @@ constexpr int kRowBytes = kBK / 2;    // 64 code bytes per row per step
 constexpr int kLdsRow = kRowBytes + 16;  // padded LDS row stride: conflict-free 16-byte reads
 constexpr int kScaleBytes = kBK / 16;    // 8 scale bytes per row per step
 constexpr size_t kDecodeMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+// In-kernel activation quantization of the decode kernel: at most this many
+// rows, and K up to kFusedMaxK.  The kernel handles up to 4 rows; at 3 and 4
+// the quantize ALU work outgrows the time the weight loads leave free, and a
+// separate quantize launch is faster (measured at N = 12288 and 12384,
+// K = 5120).
+constexpr int kFusedRows = 2, kFusedMaxK = 8192;
 
 // fp16 pair (v, v) of an E4M3 scale byte times 2^-8.
 __device__ __forceinline__ uint32_t scale_pair(uint32_t byte) {
@@ -713,6 +720,14 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
 //    are copied to LDS once, up front, in contiguous runs per row; read per
 //    tile, they cost no extra memory requests.
 //  * Rows >= M and rows >= N read zeros through the buffer bounds.
+//  * kXIn = 1 (activations not yet quantized: bf16 values with the given
+//    tensor scale, M <= kFusedRows, K <= kFusedMaxK): the ring also carries
+//    activation values, one 16-value block per lane, and every 4 / Mp tiles
+//    (Mp = M rounded up to a power of two) the wave quantizes the next 64
+//    blocks of its K range into LDS (the same per-block arithmetic as the
+//    quantize kernel, so the same bytes), and reads its A operand back in
+//    MFMA layout.  That ALU work overlaps the weight loads in flight, which
+//    bound the loop, and saves the separate quantize launch of a decode step.
 //  * The four K-quarter partial sums are added through LDS in a fixed order
 //    (deterministic), then scaled by RN32(g_a g_w) and stored.
 // MB16 = number of 16-row blocks of A (1, 2 or 4); NB = number of 16-row
@@ -720,15 +735,22 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
 template <int MB16, int NB>
 constexpr int decode_scale_rows() { return 16 * NB + 16 * MB16; }
 
-template <int MB16, int NB, int D>
+// LDS bytes per wave and per K tile of its range: scale runs of W and A,
+// plus the quantized A codes when the kernel quantizes A itself.
+template <int MB16, int NB, int kXIn>
+constexpr int decode_wave_bytes_per_tile() { return decode_scale_rows<MB16, NB>() * 16 + (kXIn ? 16 * MB16 * 128 : 0); }
+
+template <int MB16, int NB, int D, int kXIn>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const ColScales cs,
-    int M, int N, int K, void* __restrict__ y, int64_t ldy, bool out_bf16, int nt_max) {
+    int M, int N, int K, void* __restrict__ y, int64_t ldy, bool out_bf16, int nt_max,
+    const void* __restrict__ x, int64_t ldx) {
   constexpr int NW = 16 * NB;  // weight rows per workgroup
   constexpr int MA = 16 * MB16;
   constexpr int kTileBytes = 128, kTileScales = 16;  // per row, per 256-value tile
-  constexpr int kLoads = 2 * NB + 2 * MB16;          // code loads per tile
+  constexpr int kLoads = 2 * NB + (kXIn ? 0 : 2 * MB16);  // code loads per tile
+  static_assert(kXIn == 0 || (kXIn == 1 && MB16 == 1), "in-kernel quantization: bf16, M <= kFusedRows");
   static_assert(D * kLoads < 64, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) uint8_t dsmem[];
 
@@ -740,8 +762,9 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
   const int kt = K / 256;
   const int t0 = (kt * wave) / 4, nt = (kt * (wave + 1)) / 4 - t0;
   const int run = nt * kTileScales;  // scale bytes per row in this wave's range
-  uint8_t* const wsl = dsmem + wave * decode_scale_rows<MB16, NB>() * nt_max * kTileScales;  // [NW rows][run]
-  uint8_t* const asl = wsl + NW * run;                                                  // [MA rows][run]
+  uint8_t* const wsl = dsmem + wave * decode_wave_bytes_per_tile<MB16, NB, kXIn>() * nt_max;  // [NW rows][run]
+  uint8_t* const asl = wsl + NW * run;                                                    // [MA rows][run]
+  uint8_t* const acl = asl + MA * run;  // kXIn: A codes [MA rows][nt * 128]
 
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_codes, (int64_t)N * row_bytes);
   const __amdgpu_buffer_rsrc_t rws = make_rsrc(w_scales, (int64_t)N * srow_bytes);
@@ -757,11 +780,30 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
       if (u < (uint32_t)(NW * nt))
         lds_copy16(rws, (uint32_t)(n0 + row) * srow_bytes + (t0 + t) * kTileScales, 0, wsl + 64 * i * 16);
     }
-    for (int i = 0; i * 64 < MA * nt; ++i) {
-      const uint32_t u = 64 * i + lane, row = (u * inv) >> 20, t = u - row * nt;
-      if (u < (uint32_t)(MA * nt))
-        lds_copy16(ras, row * srow_bytes + (t0 + t) * kTileScales, 0, asl + 64 * i * 16);
+    if constexpr (kXIn == 0) {
+      for (int i = 0; i * 64 < MA * nt; ++i) {
+        const uint32_t u = 64 * i + lane, row = (u * inv) >> 20, t = u - row * nt;
+        if (u < (uint32_t)(MA * nt))
+          lds_copy16(ras, row * srow_bytes + (t0 + t) * kTileScales, 0, asl + 64 * i * 16);
+      }
     }
+  }
+  // kXIn: rows 0 .. Mp - 1 of A are quantized in the kernel, Mp = M rounded
+  // up to 1, 2 or 4.  One pass of the wave quantizes 64 blocks of 16 values,
+  // one per lane, covering P = 4 / Mp tiles: lane l takes block j = l % 16
+  // of row r = (l / 16) % Mp of tile t + l / (16 Mp), for the tiles t with
+  // t % P == 0.  The values travel in the ring with the weights of tile t;
+  // the other tiles carry a dummy block (row 0, tile 0: always in bounds),
+  // so the ring stays the same for every tile.  Rows M .. Mp - 1 are
+  // quantized from that dummy block and stored as zeros; rows Mp .. 15 of
+  // the A operand are cleared here, once.
+  const int lmp = M == 1 ? 0 : (M == 2 ? 1 : 2), mp = 1 << lmp, pt = 4 >> lmp;
+  const int xj = lane & 15, xr = (lane >> 4) & (mp - 1), xto = lane >> (4 + lmp);
+  const uint16_t* const x_lane = reinterpret_cast<const uint16_t*>(x) + 16 * xj;
+  if constexpr (kXIn != 0) {
+    for (int o = 16 * lane; o < (MA - mp) * nt * kTileBytes; o += 64 * 16)
+      *reinterpret_cast<u32x4_t*>(acl + mp * nt * kTileBytes + o) = u32x4_t{0, 0, 0, 0};
+    for (int o = lane; o < (MA - mp) * run; o += 64) asl[mp * run + o] = 0;
   }
 
   // per-lane code offsets at tile 0 of this wave's K range
@@ -774,6 +816,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
     a_off[i] = (uint32_t)(8 * i + (lane & 7)) * row_bytes + (uint32_t)(lane >> 3) * 16;
 
   struct Tile {
+    u32x4_t x[kXIn ? 2 : 1];  // kXIn: the lane's 16 bf16 values
     u32x4_t w[2 * NB];
     u32x4_t a[2 * MB16];
   };
@@ -786,13 +829,27 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
   auto load = [&](Tile& T, int t) {
     const bool ok = t < nt;
     const uint32_t kc = (uint32_t)(t0 + t) * kTileBytes;
+    if constexpr (kXIn != 0) {
+      const int tq = t + xto;  // the lane's tile when t starts a pass
+      const bool xok = (t & (pt - 1)) == 0 && tq < nt && xr < M;
+      const u32x4_t* p = reinterpret_cast<const u32x4_t*>(
+          xok ? x_lane + (int64_t)xr * ldx + (int64_t)(t0 + tq) * 256 : x_lane);
+      T.x[0] = p[0];
+      T.x[1] = p[1];
+    }
 #pragma unroll
     for (int i = 0; i < 2 * NB; ++i)
       T.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? w_off[i] + kc : kOutside, 0, 0);
+    if constexpr (kXIn == 0) {
 #pragma unroll
-    for (int i = 0; i < 2 * MB16; ++i)
-      T.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off[i] + kc : kOutside, 0, 0);
+      for (int i = 0; i < 2 * MB16; ++i)
+        T.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off[i] + kc : kOutside, 0, 0);
+    }
   };
+
+  // kXIn: the tensor scale of A and an approximate 1 / (6 of it)
+  const float gq = kXIn ? *a_gs : 1.0f;
+  const float r6 = __builtin_amdgcn_rcpf(6.0f * gq);
 
   floatx4_t acc[NB][MB16];
 #pragma unroll
@@ -815,6 +872,32 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
   // dequantized MFMA operands of the last three steps (see compute)
   half8_t wv[3][NB], av[3][MB16];
   auto compute = [&](const Tile& T, int t) {
+    if constexpr (kXIn != 0) {
+      // a pass: quantize the A blocks of tiles t .. t + P - 1 into LDS (codes
+      // of block j of row r of tile u at r * 128 nt + 128 u + 8 j, scale at
+      // r * run + 16 u + j); the same wave reads them back in MFMA layout
+      if (t < nt && (t & (pt - 1)) == 0) {
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[8 * k + 2 * e] = __uint_as_float(T.x[k][e] << 16);
+            v[8 * k + 2 * e + 1] = __uint_as_float(T.x[k][e] & 0xFFFF0000u);
+          }
+        uint32_t w0, w1;
+        uint32_t sc = quantize_block(v, gq, r6, w0, w1);
+        if (xr >= M) w0 = w1 = sc = 0;
+        const int tq = t + xto;
+        if (tq < nt) {
+          *reinterpret_cast<u32x2_t*>(acl + xr * (nt * kTileBytes) + tq * kTileBytes + 8 * xj) = u32x2_t{w0, w1};
+          asl[xr * run + tq * kTileScales + xj] = (uint8_t)sc;
+        }
+      }
+      // other lanes read these bytes below: keep every LDS read after the
+      // writes (a wave's LDS accesses complete in issue order)
+      __asm__ volatile("" ::: "memory");
+    }
     // scale dword of the lane (4 blocks: chunks 2g and 2g + 1); phantom
     // tiles read the last real tile's scales (their codes are zero)
     const int ts = min(t, nt - 1) * kTileScales + 4 * g;
@@ -826,8 +909,19 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
     u32x4_t wr[NB][2], ar[MB16][2];
 #pragma unroll
     for (int j = 0; j < NB; ++j) to_mfma_rows(T.w[2 * j], T.w[2 * j + 1], wr[j][0], wr[j][1]);
+    if constexpr (kXIn == 0) {
 #pragma unroll
-    for (int b = 0; b < MB16; ++b) to_mfma_rows(T.a[2 * b], T.a[2 * b + 1], ar[b][0], ar[b][1]);
+      for (int b = 0; b < MB16; ++b) to_mfma_rows(T.a[2 * b], T.a[2 * b + 1], ar[b][0], ar[b][1]);
+    } else {
+      // A already in LDS: row q, chunks 2g and 2g + 1 of the tile
+      const int tc = min(t, nt - 1) * kTileBytes + 32 * g;
+#pragma unroll
+      for (int b = 0; b < MB16; ++b) {
+        const uint8_t* p = acl + (16 * b + q) * (nt * kTileBytes) + tc;
+        ar[b][0] = *reinterpret_cast<const u32x4_t*>(p);
+        ar[b][1] = *reinterpret_cast<const u32x4_t*>(p + 16);
+      }
+    }
     // step s: chunk s / 4, dword s % 4; its scale is byte 2 (s / 4) + (s % 4) / 2
     // of the lane's scale dword.  Operands of step s + 1 are dequantized while
     // the MFMAs of step s issue, and the operands of step s - 1 are kept live
@@ -978,9 +1072,9 @@ bool allow_lds(const void* fn, size_t bytes) {
 
 // LDS bytes of a decode launch: the per-wave scale runs, or the reduction
 // buffer if larger.
-template <int MB16, int NB>
+template <int MB16, int NB, int kXIn>
 size_t decode_lds_bytes(int nt_max) {
-  const size_t scales = (size_t)4 * decode_scale_rows<MB16, NB>() * nt_max * 16;
+  const size_t scales = (size_t)4 * decode_wave_bytes_per_tile<MB16, NB, kXIn>() * nt_max;
   const size_t red = (size_t)3 * NB * MB16 * 4 * 64 * sizeof(float);
   return scales > red ? scales : red;
 }
@@ -1010,6 +1104,78 @@ hipError_t launch_tiles(const uint8_t* a_codes, const uint8_t* a_scales, const f
 
 }  // namespace
 
+namespace {
+
+// Weight blocks of 16 rows per decode workgroup: the fewest rounds of 256
+// workgroups times the blocks each one streams (ties: more blocks, so fewer
+// workgroups re-read A).
+int decode_blocks_per_wg(int64_t N) {
+  const int64_t rb = (N + 15) / 16;
+  int nb = 4;
+  int64_t best = INT64_MAX;
+  for (int c = 4; c >= 1; --c) {
+    const int64_t cost = ((rb + c - 1) / c + 255) / 256 * c;
+    if (cost < best) {
+      best = cost;
+      nb = c;
+    }
+  }
+  return nb;
+}
+
+template <int MB, int kXIn>
+size_t decode_lds_for(int nb, int nt_max) {
+  switch (nb) {
+    case 1: return decode_lds_bytes<MB, 1, kXIn>(nt_max);
+    case 2: return decode_lds_bytes<MB, 2, kXIn>(nt_max);
+    case 3: return decode_lds_bytes<MB, 3, kXIn>(nt_max);
+    default: return decode_lds_bytes<MB, 4, kXIn>(nt_max);
+  }
+}
+
+// Launches the decode kernel if the shape fits it (returns false otherwise).
+// kXIn = 0: A is NVFP4 codes and scales; 1 / 2: A is bf16 / fp32 values
+// quantized in the kernel (M <= 16).
+template <int kXIn>
+bool launch_decode(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs, const void* x, int64_t ldx,
+                   const uint8_t* w_codes, const uint8_t* w_scales, const ColScales& cs, int64_t M, int64_t N,
+                   int64_t K, void* y, bool out_bf16, int64_t ldy, hipStream_t stream, hipError_t* err) {
+  const int nt_max = (int)((K / 256 + 3) / 4);
+  const int nb = decode_blocks_per_wg(N);
+  const dim3 grid((unsigned)(((N + 15) / 16 + nb - 1) / nb)), block(256);
+  const int m = (int)M, n = (int)N, k = (int)K;
+#define NVFP4_DECODE_NB(MB, NBB, DD)                                                                              \
+  do {                                                                                                             \
+    const size_t lds = decode_lds_bytes<MB, NBB, kXIn>(nt_max);                                                    \
+    if (lds > kDecodeMaxLds || !allow_lds((const void*)gemm_decode_kernel<MB, NBB, DD, kXIn>, lds)) return false; \
+    gemm_decode_kernel<MB, NBB, DD, kXIn><<<grid, block, lds, stream>>>(                                           \
+        a_codes, a_scales, a_gs, w_codes, w_scales, cs, m, n, k, y, ldy, out_bf16, nt_max, x, ldx);                \
+    *err = hipGetLastError();                                                                                      \
+    return true;                                                                                                   \
+  } while (0)
+#define NVFP4_DECODE(MB, DD)                        \
+  do {                                              \
+    switch (nb) {                                   \
+      case 1: NVFP4_DECODE_NB(MB, 1, DD); break;    \
+      case 2: NVFP4_DECODE_NB(MB, 2, DD); break;    \
+      case 3: NVFP4_DECODE_NB(MB, 3, DD); break;    \
+      default: NVFP4_DECODE_NB(MB, 4, DD); break;   \
+    }                                               \
+  } while (0)
+  if constexpr (kXIn != 0) {
+    NVFP4_DECODE(1, 3);
+  } else {
+    if (M <= 16) NVFP4_DECODE(1, 3);
+    else if (M <= 32) NVFP4_DECODE(2, 3);
+    else NVFP4_DECODE(4, 2);
+  }
+#undef NVFP4_DECODE
+#undef NVFP4_DECODE_NB
+  return false;
+}
+
+}  // namespace
+
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
                        const uint8_t* w_codes, const uint8_t* w_scales, const ColScales& cs,
                        int64_t M, int64_t N, int64_t K, void* y, bool out_bf16, int64_t ldy,
@@ -1029,49 +1195,35 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
                                                                     (int)M, (int)N, (int)K, y, ldy);
     return hipGetLastError();
   }
-  // decode: buffer offsets of rows up to N + 47 must stay below 2^31, and
+  // decode: buffer offsets of rows up to N + 63 must stay below 2^31, and
   // the scale runs of the longest K quarter must fit in LDS
   const bool fits_decode = (N + 64) * (K / 2) < ((int64_t)1 << 31) && M * (K / 2) < ((int64_t)1 << 31);
   if (aligned && fits_decode && M <= 64 && K % 256 == 0) {
-    const int nt_max = (int)((K / 256 + 3) / 4);
-    // NB 16-row weight blocks per workgroup: the fewest rounds of 256
-    // workgroups times the blocks each one streams (ties: more blocks, so
-    // fewer workgroups re-read A)
-    const int64_t rb = (N + 15) / 16;
-    int nb = 4;
-    int64_t best = INT64_MAX;
-    for (int c = 4; c >= 1; --c) {
-      const int64_t cost = ((rb + c - 1) / c + 255) / 256 * c;
-      if (cost < best) { best = cost; nb = c; }
-    }
-    const dim3 grid((unsigned)((rb + nb - 1) / nb)), block(256);
-    const int m = (int)M, n = (int)N, k = (int)K;
-#define NVFP4_DECODE_NB(MB, NBB, DD)                                                                           \
-  do {                                                                                                          \
-    const size_t lds = decode_lds_bytes<MB, NBB>(nt_max);                                                       \
-    if (lds <= kDecodeMaxLds && allow_lds((const void*)gemm_decode_kernel<MB, NBB, DD>, lds)) {                \
-      gemm_decode_kernel<MB, NBB, DD><<<grid, block, lds, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, \
-                                                                    cs, m, n, k, y, ldy, out_bf16, nt_max);     \
-      return hipGetLastError();                                                                                 \
-    }                                                                                                           \
-  } while (0)
-#define NVFP4_DECODE(MB, DD)                  \
-  do {                                        \
-    switch (nb) {                             \
-      case 1: NVFP4_DECODE_NB(MB, 1, DD); break; \
-      case 2: NVFP4_DECODE_NB(MB, 2, DD); break; \
-      case 3: NVFP4_DECODE_NB(MB, 3, DD); break; \
-      default: NVFP4_DECODE_NB(MB, 4, DD); break; \
-    }                                         \
-  } while (0)
-    if (M <= 16) NVFP4_DECODE(1, 3);
-    else if (M <= 32) NVFP4_DECODE(2, 3);
-    else NVFP4_DECODE(4, 2);
-#undef NVFP4_DECODE
-#undef NVFP4_DECODE_NB
+    hipError_t err = hipSuccess;
+    if (launch_decode<0>(a_codes, a_scales, a_gs, nullptr, 0, w_codes, w_scales, cs, M, N, K, y, out_bf16, ldy,
+                         stream, &err))
+      return err;
   }
   return launch_tiles<128, 128, 64, 64>(a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y,
                                         out_bf16, ldy, aligned, stream);
+}
+
+bool quantize_gemm_fused_fits(int64_t M, int64_t N, int64_t K, bool in_bf16) {
+  if (!in_bf16 || M < 1 || M > kFusedRows || K % 256 != 0) return false;
+  if (K > kFusedMaxK) return false;
+  if ((N + 64) * (K / 2) >= ((int64_t)1 << 31)) return false;
+  return decode_lds_for<1, 1>(decode_blocks_per_wg(N), (int)((K / 256 + 3) / 4)) <= kDecodeMaxLds;
+}
+
+hipError_t launch_quantize_gemm_fused(const void* x, bool in_bf16, int64_t ldx, const float* a_gs,
+                                      const uint8_t* w_codes, const uint8_t* w_scales, const ColScales& cs,
+                                      int64_t M, int64_t N, int64_t K, void* y, bool out_bf16, int64_t ldy,
+                                      hipStream_t stream) {
+  hipError_t err = hipErrorInvalidValue;
+  if (!in_bf16) return hipErrorInvalidValue;
+  const bool ok = launch_decode<1>(nullptr, nullptr, a_gs, x, ldx, w_codes, w_scales, cs, M, N, K, y, out_bf16,
+                                   ldy, stream, &err);
+  return ok ? err : hipErrorInvalidConfiguration;
 }
 
 }  // namespace nvfp4

@@ -29,6 +29,15 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
                        int64_t M, int64_t N, int64_t K, void* y, bool out_bf16, int64_t ldy,
                        hipStream_t stream);
 
+// Decode GEMM with the activation quantization done inside the kernel (bf16
+// X, given tensor scale).  Only for shapes where quantize_gemm_fused_fits();
+// W pointers 16 / 8 byte aligned, X rows 16 byte aligned.
+bool quantize_gemm_fused_fits(int64_t M, int64_t N, int64_t K, bool in_bf16);
+hipError_t launch_quantize_gemm_fused(const void* x, bool in_bf16, int64_t ldx, const float* a_gs,
+                                      const uint8_t* w_codes, const uint8_t* w_scales, const ColScales& cs,
+                                      int64_t M, int64_t N, int64_t K, void* y, bool out_bf16, int64_t ldy,
+                                      hipStream_t stream);
+
 hipError_t launch_harmonize(uint8_t* scales, const float* module_gs, const int64_t* module_rows,
                             int32_t n_modules, int64_t K, float* shared_gs, uint32_t* counters,
                             hipStream_t stream);

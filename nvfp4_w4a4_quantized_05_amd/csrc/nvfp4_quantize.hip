@@ -12,76 +12,16 @@
 // wave covers 64 consecutive blocks, so every load and store instruction of
 // a wave touches one contiguous 1-2 KiB span.
 //
-// Exact rounding at fp32 cost.  The quotients are formed approximately in
-// fp32 (a reciprocal and a multiply, a few ulp of error) and rounded by the
-// hardware converters (fp8 for the scale, fp4 for the codes), which round to
-// nearest even.  That gives the exact-real answer unless the quotient lies
-// within a few ulp of a rounding midpoint.  Every midpoint of the E2M1 grid
-// has at most 2 mantissa bits, and every midpoint of the E4M3 grid at most 4,
-// so "near a midpoint" is detected from the low mantissa bits of the
-// approximate quotient (false alarms on grid points are harmless).  Only
-// then is the decision taken exactly: with the midpoint t (exact in fp32),
-// fma(t * scale, g, -|x|) is the exact difference t*scale*g - |x| rounded
-// once, so its sign (and whether it is zero: a tie) is exact.  Random data
-// hits this path for about one value in 10^5.
+// The per-block arithmetic (exact rounding at fp32 cost) is in
+// nvfp4_quant_block.h.
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
+#include "nvfp4_quant_block.h"
 
 namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr uint32_t kNearUlps = 16;  // margin (in ulps) of the near-midpoint test
-
-// Exact correction of a block-scale candidate s0 = RNE(approx(bm / (6 g))).
-__device__ __noinline__ uint32_t fix_scale(uint32_t s0, float bm, float g) {
-  if (s0 > 0) {
-    const float lo = 0.5f * (e4m3_to_f32(s0 - 1) + e4m3_to_f32(s0));  // exact midpoint
-    const float t = fmaf(lo * 6.0f, g, -bm);                          // sign of lo*6g - bm
-    if (t > 0.0f || (t == 0.0f && (s0 & 1u))) return s0 - 1;
-  }
-  if (s0 < 0x7Eu) {
-    const float hi = 0.5f * (e4m3_to_f32(s0) + e4m3_to_f32(s0 + 1));
-    const float t = fmaf(hi * 6.0f, g, -bm);
-    if (t < 0.0f || (t == 0.0f && (s0 & 1u))) return s0 + 1;
-  }
-  return s0;
-}
-
-// Exact E2M1 magnitude of |x| / (unit) when the approximate quotient y is
-// within a few ulp of a value with <= 2 mantissa bits; `hw` is the
-// hardware's magnitude code for y.  unit = val(scale), multiplied by g
-// inside the fma so that no product is rounded.
-__device__ __noinline__ uint32_t fix_code(uint32_t hw, float ax, float y, float sval, float g) {
-  const uint32_t yb = __float_as_uint(fabsf(y));
-  const uint32_t mb = (yb + 0x100000u) & ~0x1FFFFFu;  // nearest value with 2 mantissa bits
-  uint32_t lower, even;
-  switch (mb) {
-    case 0x3E800000u: lower = 0; even = 0; break;  // 0.25: 0 | 0.5
-    case 0x3F400000u: lower = 1; even = 2; break;  // 0.75: 0.5 | 1
-    case 0x3FA00000u: lower = 2; even = 2; break;  // 1.25: 1 | 1.5
-    case 0x3FE00000u: lower = 3; even = 4; break;  // 1.75: 1.5 | 2
-    case 0x40200000u: lower = 4; even = 4; break;  // 2.5: 2 | 3
-    case 0x40600000u: lower = 5; even = 6; break;  // 3.5: 3 | 4
-    case 0x40A00000u: lower = 6; even = 6; break;  // 5: 4 | 6
-    default: return hw;                            // near a grid value: no decision here
-  }
-  const float t = fmaf(__uint_as_float(mb) * sval, g, -ax);  // sign of mid*val(s)*g - |x|
-  if (t > 0.0f) return lower;
-  if (t < 0.0f) return lower + 1;
-  return even;
-}
-
-__device__ __forceinline__ bool near_e2m1_midpoint(float y) {
-  const uint32_t b = __float_as_uint(y);
-  return (((b + kNearUlps) & 0x1FFFFFu) <= 2 * kNearUlps) && ((b & 0x7FFFFFFFu) != 0u);
-}
-
-__device__ __forceinline__ bool near_e4m3_midpoint(float q) {
-  const uint32_t b = __float_as_uint(q);
-  return ((b + kNearUlps) & 0x7FFFFu) <= 2 * kNearUlps;
-}
-
 template <bool kBf16>
 __device__ __forceinline__ void load_block(const void* base, int64_t elem_off, float v[16]) {
   if constexpr (kBf16) {
@@ -126,47 +66,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   float v[16];
   load_block<kBf16>(x, off, v);
 
-  float bm = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(v[i]));
-
-  // block scale: RNE(bm / (6 g)) with saturation at 448
-  const float q = fminf(bm * r6, kE4M3Max);
-  uint32_t s = f32_to_e4m3(q);
-  if (near_e4m3_midpoint(q)) s = fix_scale(s, bm, g);
-
-  const float sval = e4m3_to_f32(s);
-  const float rcp = s ? __builtin_amdgcn_rcpf(sval * g) : 0.0f;  // zero scale: all magnitudes 0
-
-  float y[16];
-  bool near = false;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    y[i] = v[i] * rcp;
-    near |= near_e2m1_midpoint(y[i]);
-  }
-  uint32_t w0 = 0, w1 = 0;
-  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[0], y[1], 1.0f, 0);
-  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[2], y[3], 1.0f, 1);
-  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[4], y[5], 1.0f, 2);
-  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[6], y[7], 1.0f, 3);
-  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[8], y[9], 1.0f, 0);
-  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[10], y[11], 1.0f, 1);
-  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[12], y[13], 1.0f, 2);
-  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[14], y[15], 1.0f, 3);
-
-  if (near) {  // rare: settle values next to an E2M1 midpoint exactly
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (near_e2m1_midpoint(y[i])) {
-        uint32_t& w = i < 8 ? w0 : w1;
-        const int sh = 4 * (i & 7);
-        const uint32_t hw = (w >> sh) & 7u;
-        const uint32_t mag = fix_code(hw, fabsf(v[i]), y[i], sval, g);
-        w = (w & ~(7u << sh)) | (mag << sh);
-      }
-    }
-  }
+  uint32_t w0, w1;
+  const uint32_t s = quantize_block(v, g, r6, w0, w1);
   u32x2_t out;
   out[0] = w0;
   out[1] = w1;

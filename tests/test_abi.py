@@ -122,6 +122,43 @@ def test_gemm_segmented_rejects_bad_arguments(lib):
     assert lib.nvfp4_last_hip_error() == 0
 
 
+def qg(lib, x=P16, dt=1, ldx=256, a_gs=P16, ptrs=None, M=2, N=64, K=256, y=P16, od=1, ldy=64,
+       ws=None, ws_bytes=0):
+    p = ptrs or [P16] * 3
+    return lib.nvfp4_quantize_gemm(x, dt, ldx, a_gs, *p, M, N, K, y, od, ldy, ws, ws_bytes, None)
+
+
+def test_quantize_gemm_rejects_bad_arguments_and_sizes_its_workspace(lib):
+    assert qg(lib, dt=3) == DTYPE
+    assert qg(lib, od=4) == DTYPE
+    assert qg(lib, K=40, ldx=40) == SHAPE
+    assert qg(lib, ldx=128) == SHAPE
+    assert qg(lib, ldy=32) == SHAPE
+    assert qg(lib, M=-1) == SHAPE
+    assert qg(lib, x=None) == NULL
+    assert qg(lib, a_gs=None) == NULL
+    for i in range(3):
+        p = [P16] * 3
+        p[i] = None
+        assert qg(lib, ptrs=p) == NULL
+    assert qg(lib, y=None) == NULL
+    assert qg(lib, x=P_ODD) == ALIGN
+    assert qg(lib, ldx=260) == ALIGN                          # bf16 row stride of 520 bytes
+    assert qg(lib, M=0, x=None, a_gs=None, ptrs=[None] * 3, y=None) == OK
+    # decode-sized: one kernel, no workspace; larger M or K: codes + scales
+    assert lib.nvfp4_quantize_gemm_workspace_size(1, 12288, 5120, 1, 1) == 0
+    assert lib.nvfp4_quantize_gemm_workspace_size(2, 12384, 4096, 1, 0) == 0
+    assert lib.nvfp4_quantize_gemm_workspace_size(3, 12384, 4096, 1, 0) == 3 * 2048 + 3 * 256  # M > 2
+    assert lib.nvfp4_quantize_gemm_workspace_size(5, 12384, 4096, 1, 0) == 5 * 2048 + 5 * 256
+    assert lib.nvfp4_quantize_gemm_workspace_size(1, 12288, 5120, 0, 1) == 2560 + 320     # fp32 activations
+    assert lib.nvfp4_quantize_gemm_workspace_size(40, 12288, 5120, 1, 1) == 40 * 2560 + 40 * 320
+    assert lib.nvfp4_quantize_gemm_workspace_size(3, 100, 1040, 0, 1) == 1792 + 3 * 65   # K % 256 != 0
+    assert lib.nvfp4_quantize_gemm_workspace_size(2, 12288, 17408, 1, 1) == 17408 + 2 * 1088  # K > 8192
+    assert qg(lib, M=40, N=64, K=256, ws_bytes=40 * 128 + 40 * 16 - 1, ws=P16) == WORKSPACE
+    assert qg(lib, M=40, N=64, K=256, ws_bytes=1 << 20, ws=None) == NULL
+    assert lib.nvfp4_last_hip_error() == 0
+
+
 def h(lib, scales=P16, mgs=P16, rows=(8, 4), K=32, sgs=ctypes.c_void_p(0x20000), counters=None):
     arr = (ctypes.c_int64 * len(rows))(*rows)
     return lib.nvfp4_harmonize_fused_scales(scales, mgs, arr, len(rows), K, sgs, counters, None)

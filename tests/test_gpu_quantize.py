@@ -115,6 +115,45 @@ def test_near_ties_of_scales():
         assert_codes_equal(c, s, wc, ws, f"E4M3 near ties g={g}")
 
 
+def bf16_tie_blocks(g):
+    """16-value blocks of bf16-exact values on and next to the rounding
+    midpoints, for a power-of-two tensor scale g: per block scale s, a block
+    maximum 6 val(s) g (scale quotient exactly val(s)), the unit val(s) g, the
+    E2M1 midpoints times that unit, and their bf16 neighbours; then blocks whose
+    maximum sits on, or next to, an E4M3 midpoint times 6 g.  bf16 data
+    reaches exact ties this way (short mantissas), unlike random fp32."""
+    def bf16_step(v, d):
+        b = np.array([v], np.float32).view(np.uint32)[0] >> 16
+        return np.array([(int(b) + d) << 16], np.uint32).view(np.float32)[0]
+    blocks = []
+    for s in list(range(8, 0x7F, 5)) + [0x7E]:
+        unit = np.float32(ref.E4M3_VALUES[s] * np.float64(g))
+        mids = [np.float32(m * unit) for m in ref.E2M1_MIDPOINTS]
+        blocks.append([np.float32(6 * unit), unit] + mids + [bf16_step(m, -1) for m in mids[:4]]
+                      + [bf16_step(m, 1) for m in mids[4:]])
+        blocks.append([-np.float32(6 * unit), -unit] + [bf16_step(m, 1) for m in mids] + [-m for m in mids[:4]]
+                      + [bf16_step(-m, 1) for m in mids[4:]])
+    for mid in ref.E4M3_MIDPOINTS[::4]:
+        t = np.float32(mid * 6.0 * np.float64(g))
+        for v in (t, bf16_step(t, -1), bf16_step(t, 1)):
+            r = [np.float32(0)] * 16
+            r[3] = v
+            r[9] = -v / np.float32(4)
+            blocks.append(r)
+    x = np.array(blocks, np.float32)
+    assert np.array_equal(torch.from_numpy(x).to(torch.bfloat16).float().numpy(), x)  # exact in bf16
+    return x
+
+
+def test_exact_ties_in_bf16_input():
+    need_gpu()
+    for g in (np.float32(1.0), np.float32(2.0 ** -7), np.float32(0.5)):
+        x = bf16_tie_blocks(g)
+        c, s, _ = _gq(torch.from_numpy(x).to(torch.bfloat16).cuda(), float(g))
+        wc, ws, _ = ref.quantize(x, g=g)
+        assert_codes_equal(c, s, wc, ws, f"bf16 exact ties g={g}")
+
+
 def test_tensor_scale_from_amax_many_magnitudes():
     need_gpu()
     gen = torch.Generator().manual_seed(3)

@@ -1,0 +1,109 @@
+"""nvfp4_quantize_gemm: quantize (given tensor scale) + GEMM in one call.
+The one-kernel decode path and the workspace path must both give the same
+bytes as nvfp4_quantize followed by nvfp4_gemm, and agree with the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_w4a4_quantized_05_amd as nv
+from oracle import nvfp4_ref as ref
+from tests.gpu_util import assert_codes_equal, assert_gemm_close, host_f32, need_gpu
+from tests.test_gpu_quantize import bf16_tie_blocks
+from workloads import activations, normal_weights
+
+pytestmark = pytest.mark.gpu
+
+
+def _weights(N, K, seed):
+    w = normal_weights(N, K, 0.02, seed=seed, device="cuda")
+    return nv.quantize(w)
+
+
+def _two_calls(x, g, wq, out_dtype):
+    a = nv.quantize(x, g, from_amax=False)
+    return nv.gemm(*a, *wq, out_dtype=out_dtype)
+
+
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("N", [100, 5120, 12288, 12384])
+@pytest.mark.parametrize("K", [5120, 8192])
+def test_one_kernel_path_is_bit_identical_to_two_calls(M, N, K):
+    need_gpu()
+    print(f"[quantize_gemm] fused M={M} N={N} K={K}", flush=True)
+    lib = nv.load()
+    assert lib.nvfp4_quantize_gemm_workspace_size(M, N, K, 1, 1) == 0
+    x = activations("t3_outlier1pct", M, K, seed=M + N, device="cuda")
+    g = nv.quantize(x)[2].clone()
+    wq = _weights(N, K, seed=N)
+    for od in (torch.bfloat16, torch.float32):
+        y = nv.quantize_gemm(x, g, *wq, out_dtype=od)
+        y2 = _two_calls(x, g, wq, od)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2), f"M={M} N={N} {od}"
+
+
+@pytest.mark.parametrize("shape", [(40, 12288, 5120), (5, 12288, 5120), (4, 12384, 5120), (3, 12288, 8192),
+                                   (2, 12288, 17408), (3, 100, 1040), (300, 700, 384)])
+def test_workspace_path_is_bit_identical_to_two_calls(shape):
+    need_gpu()
+    M, N, K = shape
+    print(f"[quantize_gemm] workspace M={M} N={N} K={K}", flush=True)
+    assert nv.load().nvfp4_quantize_gemm_workspace_size(M, N, K, 1, 1) > 0
+    x = activations("t3_outlier1pct", M, K, seed=M * 7 + K, device="cuda")
+    g = nv.quantize(x)[2].clone()
+    wq = _weights(N, K, seed=K)
+    y = nv.quantize_gemm(x, g, *wq, out_dtype=torch.bfloat16)
+    y2 = _two_calls(x, g, wq, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_row_stride_and_input_dtype_against_the_oracle(dtype):
+    """Activations read with a row stride (bf16: one kernel; fp32: workspace
+    path), against the oracle: quantized A from the oracle's quantizer,
+    tolerance on the GEMM."""
+    need_gpu()
+    M, N, K = 2, 5120, 1024
+    xs = activations("t3_outlier1pct", M, 2 * K, seed=11, device="cuda", dtype=dtype)
+    x = xs[:, :K]                              # row stride 2K
+    g = nv.quantize(x.contiguous())[2].clone()
+    wq = _weights(N, K, seed=12)
+    fused = nv.load().nvfp4_quantize_gemm_workspace_size(M, N, K, 1 if dtype == torch.bfloat16 else 0, 0) == 0
+    assert fused == (dtype == torch.bfloat16)
+    y = nv.quantize_gemm(x, g, *wq, out_dtype=torch.float32)
+    y2 = _two_calls(x.contiguous(), g, wq, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    oa = ref.quantize(host_f32(x.contiguous()), g=np.float32(g.item()))
+    a = nv.quantize(x.contiguous(), g, from_amax=False)
+    assert_codes_equal(a[0], a[1], oa[0], oa[1], f"strided X {dtype}")
+    wh = (wq[0].cpu().numpy(), wq[1].cpu().numpy(), np.float32(wq[2].item()))
+    Y, S = ref.gemm_ref(*oa, *wh)
+    assert_gemm_close(y, Y, S, f"quantize_gemm {dtype} X")
+
+
+def test_one_kernel_path_on_exact_ties():
+    """bf16 rows made of blocks on and next to rounding midpoints (see
+    bf16_tie_blocks): the in-kernel quantization must settle every tie as the
+    quantize kernel does, which the oracle pins bit for bit."""
+    need_gpu()
+    g = np.float32(2.0 ** -7)
+    blocks = bf16_tie_blocks(g)
+    M, K, N = 2, 2048, 5120
+    reps = -(-M * K // 16 // blocks.shape[0])
+    x = np.tile(blocks, (reps, 1))[: M * K // 16].reshape(M, K)
+    xt = torch.from_numpy(x).to(torch.bfloat16).cuda()
+    gt = torch.tensor([g], dtype=torch.float32, device="cuda")
+    assert nv.load().nvfp4_quantize_gemm_workspace_size(M, N, K, 1, 0) == 0
+    wq = _weights(N, K, seed=21)
+    y = nv.quantize_gemm(xt, gt, *wq, out_dtype=torch.float32)
+    y2 = _two_calls(xt, gt, wq, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    oa = ref.quantize(x, g=g)
+    a = nv.quantize(xt, gt, from_amax=False)
+    assert_codes_equal(a[0], a[1], oa[0], oa[1], "tie rows")
+    wh = (wq[0].cpu().numpy(), wq[1].cpu().numpy(), np.float32(wq[2].item()))
+    Y, S = ref.gemm_ref(*oa, *wh)
+    assert_gemm_close(y, Y, S, "quantize_gemm tie rows")
