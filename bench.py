@@ -110,9 +110,12 @@ def main():
 
     # ---------------- setup (untimed): weights, harmonization, inputs -------
     wq = {}
+    w_gates = {}  # unquantized a and b projections, for the gate error measurement
     for i, p in enumerate(cfg["projections"]):
         w = normal_weights(p.n, p.k, p.std, seed=seed * 100 + i, device=dev)
         wq[p.name] = nv.quantize(w)
+        if p.name in ("a", "b"):
+            w_gates[p.name] = w.cpu().numpy().astype(np.float64)
         del w
     fused = ["qkv", "z", "a", "b"]
     in_codes = torch.cat([wq[n][0] for n in fused])
@@ -219,6 +222,12 @@ def main():
     extra = {} if args.no_extras else extra_measurements(nv, torch, np, dev, stream, xs, calib, qbuf, ys, in_codes,
                                                          in_scales, in_gs, in_scales_modules, module_gs,
                                                          [P[n].n for n in fused], T)
+    if not args.no_extras:
+        extra["gate_error_compression"] = gate_error_compression(nv, torch, np, dev, xs[0], calib[0], wq, w_gates,
+                                                                 seed)
+        extra["in_proj_gates_epilogue"] = gates_epilogue_timing(nv, torch, np, dev, stream, qbuf[0], calib[0],
+                                                                in_codes, in_scales_modules, module_gs,
+                                                                [P[n].n for n in fused], ys[0], seed, T)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -342,6 +351,87 @@ def extra_measurements(nv, torch, np, dev, stream, xs, calib, qbuf, ys, in_codes
     out["decode_quantize_gemm_in_proj_12384x5120"] = qg
     del copies, hcopies
     return out
+
+
+def gdn_gate_params(np, n, seed):
+    """Synthetic per-head GDN gate parameters: A ~ U(1, 16), A_log = log A;
+    dt ~ exp(U(log 1e-3, log 1e-1)), dt_bias = its inverse softplus."""
+    rng = np.random.default_rng(seed)
+    a_log = np.log(rng.uniform(1.0, 16.0, n)).astype(np.float32)
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), n))
+    return a_log, (dt + np.log(-np.expm1(-dt))).astype(np.float32)
+
+
+def gate_error_compression(nv, torch, np, dev, x, g_x, wq, w_gates, seed, rows=2048):
+    """How much of the a / b projections' GEMM error reaches the gates: the
+    NVFP4 W4A4 GEMM with the gate epilogue (decay gate g on a, write
+    strength beta on b) against the unquantized model (bf16 activations,
+    fp32 weights, everything in fp64 on the host), as relative L2 errors
+    over the first `rows` tokens."""
+    n_a, n_b = w_gates["a"].shape[0], w_gates["b"].shape[0]
+    a_log, dt_bias = gdn_gate_params(np, n_a, seed + 17)
+    xr = x[:rows]
+    ac, as_, _ = nv.quantize(xr, g_x, from_amax=False)
+    wc = torch.cat([wq["a"][0], wq["b"][0]])
+    wsc = torch.cat([wq["a"][1], wq["b"][1]])
+    mgs = torch.cat([wq["a"][2], wq["b"][2]])
+    v_q = nv.gemm_segmented(ac, as_, g_x, wc, wsc, mgs, [n_a, n_b]).cpu().numpy().astype(np.float64)
+    gates_q = nv.gemm_segmented_gates(ac, as_, g_x, wc, wsc, mgs, [n_a, n_b], decay_module=0,
+                                      a_log=torch.from_numpy(a_log).to(dev), dt_bias=torch.from_numpy(dt_bias).to(dev),
+                                      write_module=1).cpu().numpy().astype(np.float64)
+    xh = xr.float().cpu().numpy().astype(np.float64)
+    v_ref = xh @ np.concatenate([w_gates["a"], w_gates["b"]]).T
+
+    def softplus(z):
+        return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+    def rel(u, v):
+        return float(np.linalg.norm(u - v) / np.linalg.norm(v))
+
+    g_ref = -np.exp(a_log.astype(np.float64)) * softplus(v_ref[:, :n_a] + dt_bias.astype(np.float64))
+    beta_ref = 1.0 / (1.0 + np.exp(-v_ref[:, n_a:]))
+    g_q, beta_q = gates_q[:, :n_a], gates_q[:, n_a:]
+    return {
+        "rows": rows,
+        "params": "A_log = log U(1,16); dt_bias = softplus^-1(exp(U(log 1e-3, log 1e-1))); seeded",
+        "a": {"gemm_rel_err": round(rel(v_q[:, :n_a], v_ref[:, :n_a]), 4),
+              "decay_g_rel_err": round(rel(g_q, g_ref), 4),
+              "forget_alpha_rel_err": round(rel(np.exp(g_q), np.exp(g_ref)), 5)},
+        "b": {"gemm_rel_err": round(rel(v_q[:, n_a:], v_ref[:, n_a:]), 4),
+              "write_beta_rel_err": round(rel(beta_q, beta_ref), 4)},
+    }
+
+
+def gates_epilogue_timing(nv, torch, np, dev, stream, q, g_x, in_codes, in_scales_modules, module_gs, module_rows,
+                          y, seed, T):
+    """The fused in-projection GEMM (segmented epilogue) with and without the
+    gate functions on its a and b columns, at the step's token count."""
+    a_log, dt_bias = gdn_gate_params(np, module_rows[2], seed + 17)
+    al, db = torch.from_numpy(a_log).to(dev), torch.from_numpy(dt_bias).to(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def plain():
+        nv.gemm_segmented(q[0], q[1], g_x, in_codes, in_scales_modules, module_gs, module_rows,
+                          out_dtype=torch.bfloat16, out=y)
+
+    def gated():
+        nv.gemm_segmented_gates(q[0], q[1], g_x, in_codes, in_scales_modules, module_gs, module_rows,
+                                out_dtype=torch.bfloat16, out=y, decay_module=2, a_log=al, dt_bias=db,
+                                write_module=3)
+
+    # interleaved rounds, best of each: clocks drift over a run
+    best = {"segmented_ms": float("inf"), "segmented_gates_ms": float("inf")}
+    for _ in range(4):
+        for label, fn in (("segmented_ms", plain), ("segmented_gates_ms", gated)):
+            fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(5):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best[label] = min(best[label], e0.elapsed_time(e1) / 5)
+    return {k: round(v, 4) for k, v in best.items()}
 
 
 def cpu_baseline(rows, xs, gemms, wq, fused, P, seed):

@@ -158,6 +158,41 @@ NVFP4_API nvfp4_status_t nvfp4_gemm_segmented(const uint8_t* a_codes, const uint
                                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nvfp4_gemm_segmented_gates -- nvfp4_gemm_segmented whose epilogue also
+ * evaluates the Gated DeltaNet gates on two of the modules: the log-space
+ * decay gate g = -exp(A_log) softplus(a + dt_bias) (picx.dev summary page,
+ * "Introduction and Theoretical Foundation" > "Gated DeltaNet Mechanics")
+ * and the sigmoid write strength beta = sigmoid(b) (dmarx anthology record
+ * LIT-800, "Key takeaways", gates bullet).  With v the module's output
+ * RN32(g_a g_i) * deq(A) * deq(W_i)^T (an fp32 value), column j of module
+ * `decay_module` becomes -exp(a_log[j]) * softplus(v + dt_bias[j]) and every
+ * column of module `write_module` becomes sigmoid(v); other modules are
+ * exactly as nvfp4_gemm_segmented writes them.  The gates are evaluated in
+ * fp32 with the ROCm device library's expf and log1pf, before the output
+ * conversion.
+ *
+ *   ... as for nvfp4_gemm_segmented, plus
+ *   decay_module   index of the decay-gate module (the a projection), or -1
+ *   a_log, dt_bias device, module_rows[decay_module] floats each (read);
+ *                  may be NULL when decay_module is -1
+ *   write_module   index of the write-strength module (the b projection),
+ *                  or -1; different from decay_module unless both are -1
+ * NVFP4_ERR_SHAPE for a module index outside -1 .. n_modules - 1 or equal
+ * indices; NVFP4_ERR_NULL / NVFP4_ERR_ALIGN (4 bytes) for the gate
+ * parameters; other errors as for nvfp4_gemm_segmented.  Accuracy: the
+ * GEMM's bound carried through the gate (|d/dv| <= exp(a_log[j]) for the
+ * decay, 1/4 for sigmoid) plus a few fp32 ulp of the gate.
+ */
+NVFP4_API nvfp4_status_t nvfp4_gemm_segmented_gates(const uint8_t* a_codes, const uint8_t* a_scales,
+                                                    const float* a_gs, const uint8_t* w_codes,
+                                                    const uint8_t* w_scales, const float* module_gs,
+                                                    const int64_t* module_rows, int32_t n_modules,
+                                                    int32_t decay_module, const float* a_log,
+                                                    const float* dt_bias, int32_t write_module, int64_t M,
+                                                    int64_t K, void* y, int32_t out_dtype, int64_t ldy,
+                                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * nvfp4_quantize_gemm -- quantize the activations with a given (calibrated)
  * tensor scale and multiply: y = nvfp4_gemm(nvfp4_quantize(x, a_gs), W), in
  * one call.  The activation quantization and the linear layer are the ones

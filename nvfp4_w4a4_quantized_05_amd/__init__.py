@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     Nvfp4Error,
     gemm,
     gemm_segmented,
+    gemm_segmented_gates,
     harmonize_fused_scales,
     load,
     quantize,

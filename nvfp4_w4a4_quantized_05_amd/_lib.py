@@ -22,7 +22,8 @@ SCALE_GIVEN, SCALE_FROM_AMAX = 0, 1
 STATUS_NAMES = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_DTYPE",
                 4: "NVFP4_ERR_MODE", 5: "NVFP4_ERR_ALIGN", 6: "NVFP4_ERR_WORKSPACE",
                 7: "NVFP4_ERR_HIP", 8: "NVFP4_ERR_ALIAS"}
-EXPORTS = ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_segmented", "nvfp4_quantize_gemm",
+EXPORTS = ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_segmented", "nvfp4_gemm_segmented_gates",
+           "nvfp4_quantize_gemm",
            "nvfp4_quantize_gemm_workspace_size", "nvfp4_harmonize_fused_scales",
            "nvfp4_gemm_workspace_size", "nvfp4_status_string", "nvfp4_last_hip_error")
 
@@ -55,6 +56,9 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_gemm_segmented.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(i64), i32, i64, i64, vp, i32,
                                          i64, vp, sz, vp]
     lib.nvfp4_gemm_segmented.restype = i32
+    lib.nvfp4_gemm_segmented_gates.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(i64), i32, i32, vp, vp, i32,
+                                               i64, i64, vp, i32, i64, vp, sz, vp]
+    lib.nvfp4_gemm_segmented_gates.restype = i32
     lib.nvfp4_quantize_gemm.argtypes = [vp, i32, i64, vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp, sz, vp]
     lib.nvfp4_quantize_gemm.restype = i32
     lib.nvfp4_quantize_gemm_workspace_size.argtypes = [i64, i64, i64, i32, i32]
@@ -181,6 +185,46 @@ def gemm_segmented(a_codes, a_scales, a_gs, w_codes, w_scales, module_gs, module
                                   _ptr(module_gs.contiguous()), host_rows, len(rows), M, K, _ptr(out), od,
                                   out.stride(0), _ptr(ws), ws_bytes, _stream(stream))
     _check(st, "nvfp4_gemm_segmented")
+    return out
+
+
+def gemm_segmented_gates(a_codes, a_scales, a_gs, w_codes, w_scales, module_gs, module_rows, *,
+                         decay_module: int = -1, a_log: torch.Tensor | None = None,
+                         dt_bias: torch.Tensor | None = None, write_module: int = -1,
+                         out_dtype=torch.float32, out: torch.Tensor | None = None, stream=None):
+    """gemm_segmented whose epilogue turns module `decay_module` into the decay
+    gate -exp(a_log) softplus(v + dt_bias) and module `write_module` into
+    sigmoid(v) (-1: none)."""
+    _need_gpu(a_codes, a_scales, a_gs, w_codes, w_scales, module_gs, a_log, dt_bias, out)
+    rows = [int(r) for r in module_rows]
+    M = a_codes.shape[0]
+    N = w_codes.shape[0]
+    K = a_codes.shape[1] * 2
+    if sum(rows) != N or module_gs.numel() != len(rows) or module_gs.dtype != torch.float32:
+        raise ValueError("module_rows must sum to the weight rows, one float32 scale per module")
+    if w_codes.shape[1] * 2 != K or a_scales.shape != (M, K // 16) or w_scales.shape != (N, K // 16):
+        raise ValueError("operand shapes disagree")
+    for t in (a_codes, a_scales, w_codes, w_scales):
+        if not t.is_contiguous() or t.dtype != torch.uint8:
+            raise ValueError("codes and scales must be contiguous uint8")
+    if decay_module >= 0:
+        for t in (a_log, dt_bias):
+            if t is None or t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != rows[decay_module]:
+                raise ValueError("a_log and dt_bias: contiguous float32, one per decay-module row")
+    od = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[out_dtype]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    if out.dtype != out_dtype or out.stride(1) != 1:
+        raise ValueError("out must have unit column stride and dtype out_dtype")
+    lib = load()
+    ws_bytes = lib.nvfp4_gemm_workspace_size(M, N, K, od)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a_codes.device) if ws_bytes else None
+    host_rows = (ctypes.c_int64 * len(rows))(*rows)
+    st = lib.nvfp4_gemm_segmented_gates(_ptr(a_codes), _ptr(a_scales), _ptr(a_gs), _ptr(w_codes), _ptr(w_scales),
+                                        _ptr(module_gs.contiguous()), host_rows, len(rows), decay_module,
+                                        _ptr(a_log), _ptr(dt_bias), write_module, M, K, _ptr(out), od,
+                                        out.stride(0), _ptr(ws), ws_bytes, _stream(stream))
+    _check(st, "nvfp4_gemm_segmented_gates")
     return out
 
 

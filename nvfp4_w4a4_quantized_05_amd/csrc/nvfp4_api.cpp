@@ -112,6 +112,42 @@ nvfp4_status_t nvfp4_gemm_segmented(const uint8_t* a_codes, const uint8_t* a_sca
   }
 }
 
+nvfp4_status_t nvfp4_gemm_segmented_gates(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                                          const uint8_t* w_codes, const uint8_t* w_scales,
+                                          const float* module_gs, const int64_t* module_rows, int32_t n_modules,
+                                          int32_t decay_module, const float* a_log, const float* dt_bias,
+                                          int32_t write_module, int64_t M, int64_t K, void* y, int32_t out_dtype,
+                                          int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (!module_rows) return NVFP4_ERR_NULL;
+    if (n_modules < 1 || n_modules > nvfp4::kMaxModules) return NVFP4_ERR_SHAPE;
+    if (decay_module < -1 || decay_module >= n_modules || write_module < -1 || write_module >= n_modules)
+      return NVFP4_ERR_SHAPE;
+    if (decay_module >= 0 && decay_module == write_module) return NVFP4_ERR_SHAPE;
+    if (decay_module >= 0) {
+      if (!a_log || !dt_bias) return NVFP4_ERR_NULL;
+      if (!aligned(a_log, 4) || !aligned(dt_bias, 4)) return NVFP4_ERR_ALIGN;
+    }
+    nvfp4::ColScales cs{};
+    cs.gs = module_gs;
+    cs.n = n_modules;
+    int64_t N = 0;
+    for (int32_t i = 0; i < n_modules; ++i) {
+      if (module_rows[i] < 0 || module_rows[i] > (int64_t)INT_MAX - N) return NVFP4_ERR_SHAPE;
+      if (i == decay_module) cs.decay_lo = (int)N, cs.decay_hi = (int)(N + module_rows[i]);
+      if (i == write_module) cs.write_lo = (int)N, cs.write_hi = (int)(N + module_rows[i]);
+      N += module_rows[i];
+      cs.end[i] = (int)N;
+    }
+    cs.a_log = a_log;
+    cs.dt_bias = dt_bias;
+    return gemm_checked(a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y, out_dtype, ldy,
+                        workspace_bytes, stream);
+  } catch (...) {
+    return NVFP4_ERR_HIP;
+  }
+}
+
 size_t nvfp4_quantize_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t in_dtype, int32_t out_dtype) {
   (void)out_dtype;
   if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0 || M > INT_MAX || K > INT_MAX) return 0;

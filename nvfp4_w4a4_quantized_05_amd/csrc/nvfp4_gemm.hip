@@ -108,6 +108,28 @@ __device__ __forceinline__ float col_alpha(float g_a, const ColScales& cs, int c
   return g_a * cs.gs[col_range(cs, col)];
 }
 
+// Whether output columns [c0, c1] meet a gate column range.
+__device__ __forceinline__ bool cols_gated(const ColScales& cs, int c0, int c1) {
+  return (c0 < cs.decay_hi && c1 >= cs.decay_lo) || (c0 < cs.write_hi && c1 >= cs.write_lo);
+}
+
+// Gate function of output column `col` applied to v = acc RN32(g_a g_w):
+// the decay gate g = -exp(A_log) softplus(a + dt_bias) of the picx.dev
+// summary page ("Introduction and Theoretical Foundation" > "Gated DeltaNet
+// Mechanics") and the sigmoid write strength beta = sigmoid(b) (dmarx
+// anthology record LIT-800, "Key takeaways", gates bullet).  fp32, with the
+// device library's expf and log1pf; softplus(z) = max(z, 0) +
+// log1p(exp(-|z|)) does not overflow.
+__device__ __forceinline__ float col_gate(const ColScales& cs, int col, float v) {
+  if (col >= cs.decay_lo && col < cs.decay_hi) {
+    const int j = col - cs.decay_lo;
+    const float z = v + cs.dt_bias[j];
+    return -expf(cs.a_log[j]) * (fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z))));
+  }
+  if (col >= cs.write_lo && col < cs.write_hi) return 1.0f / (1.0f + expf(-v));
+  return v;
+}
+
 template <bool kAligned>
 __device__ __forceinline__ u32x4_t load_codes16(const uint8_t* row_ptr, int64_t byte_off, int64_t row_bytes,
                                                bool row_ok) {
@@ -301,8 +323,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(
     __syncthreads();
   }
 
-  // epilogue: y = acc * RN32(g_a g_w) with the column's g_w
+  // epilogue: y = acc * RN32(g_a g_w) with the column's g_w (then the
+  // column's gate function, if any)
   const float g_a = *a_gs;
+  const bool gated = cols_gated(cs, n0, n0 + BN - 1);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -314,7 +338,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(
       for (int v = 0; v < 16; ++v) {
         const int row = m0 + wave_m * WM + i * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
         if (row < M) {
-          const float o = acc[i][j][v] * alpha;
+          float o = acc[i][j][v] * alpha;
+          if (gated) o = col_gate(cs, col, o);
           if constexpr (kOutBf16) {
             reinterpret_cast<__bf16*>(y)[(int64_t)row * ldy + col] = (__bf16)o;
           } else {
@@ -378,7 +403,7 @@ __device__ __forceinline__ int chunk_swizzle(int row) { return ((row >> 1) ^ (ro
 //   accumulators hold 4 consecutive output columns of one row: the epilogue
 //   stages rows in LDS with 8-byte writes and stores 16-byte row chunks.
 // Rows past M or N read a clamped (valid) row; their outputs are never stored.
-template <int STAGES, bool kOutBf16>
+template <int STAGES, bool kOutBf16, bool kGates>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const ColScales cs,
@@ -632,6 +657,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     alpha_tab[lane] = col_alpha(g_a, cs, c_first + lane);
     alpha_tab[lane + 64] = col_alpha(g_a, cs, c_first + lane + 64);
   }
+  // kGates: the wave's columns meet a gate range (instantiated only for
+  // GEMMs that have one, so the plain epilogue is unchanged)
+  const bool gated = kGates && cols_gated(cs, c_first, c_last);
   {
     uint8_t* strip = smem + STAGES * kStageBytes + wave * kStripBytes;
     constexpr int kChunksPerRow = WN * kEsz / 16;
@@ -648,17 +676,23 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
             for (int g = 0; g < 4; ++g) {
               const int col = j * 32 + g * 8 + half * 4;
               const floatx4_t al = *reinterpret_cast<const floatx4_t*>(alpha_tab + col);
+              floatx4_t f;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) f[t] = acc[j][i][4 * g + t] * al[t];
+              if constexpr (kGates) {
+                if (gated) {
+#pragma unroll
+                  for (int t = 0; t < 4; ++t) f[t] = col_gate(cs, c_first + col + t, f[t]);
+                }
+              }
               if constexpr (kOutBf16) {
                 typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
                 bf4_t o;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) o[t] = (__bf16)(acc[j][i][4 * g + t] * al[t]);
+                for (int t = 0; t < 4; ++t) o[t] = (__bf16)f[t];
                 *reinterpret_cast<bf4_t*>(rowp + col * kEsz) = o;
               } else {
-                floatx4_t o;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) o[t] = acc[j][i][4 * g + t] * al[t];
-                *reinterpret_cast<floatx4_t*>(rowp + col * kEsz) = o;
+                *reinterpret_cast<floatx4_t*>(rowp + col * kEsz) = f;
               }
             }
         }
@@ -1020,6 +1054,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
     const float g_a = *a_gs;
     const int s_first = col_range(cs, n0), s_last = col_range(cs, min(n0 + NW, N) - 1);
     const float alpha_u = g_a * cs.gs[s_first];
+    const bool gated = cols_gated(cs, n0, n0 + NW - 1);
     const bool vec_ok = (ldy % 4 == 0) && ((uintptr_t)y % 16 == 0);
 #pragma unroll
     for (int j = 0; j < NB; ++j)
@@ -1034,6 +1069,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
 #pragma unroll
           for (int w = 0; w < 3; ++w) t += red[((w * NB + j) * MB16 + b) * 256 + v * 64 + lane];
           o[v] = t * (s_first == s_last ? alpha_u : col_alpha(g_a, cs, n + v));
+          if (gated) o[v] = col_gate(cs, n + v, o[v]);
         }
         if (m < M) {
           if (out_bf16) {
@@ -1187,12 +1223,19 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   if (aligned && fits32 && big_tiles >= 256) {
     constexpr int kStages = 3;
     const dim3 grid((unsigned)big_tiles), block(256);
-    if (out_bf16)
-      gemm_stream_kernel<kStages, true><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, cs,
-                                                                   (int)M, (int)N, (int)K, y, ldy);
-    else
-      gemm_stream_kernel<kStages, false><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, cs,
-                                                                    (int)M, (int)N, (int)K, y, ldy);
+    const bool gates = cs.decay_hi > cs.decay_lo || cs.write_hi > cs.write_lo;
+#define NVFP4_STREAM(BF16, GATES)                                                                    \
+  gemm_stream_kernel<kStages, BF16, GATES><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, \
+                                                                       w_scales, cs, (int)M, (int)N,  \
+                                                                       (int)K, y, ldy)
+    if (out_bf16) {
+      if (gates) NVFP4_STREAM(true, true);
+      else NVFP4_STREAM(true, false);
+    } else {
+      if (gates) NVFP4_STREAM(false, true);
+      else NVFP4_STREAM(false, false);
+    }
+#undef NVFP4_STREAM
     return hipGetLastError();
   }
   // decode: buffer offsets of rows up to N + 63 must stay below 2^31, and

@@ -22,6 +22,13 @@ struct ColScales {
   const float* gs;
   int n;
   int end[kMaxModules];
+  // Gated DeltaNet gate columns (both ranges empty in a plain GEMM).  With
+  // v = acc * RN32(g_a g_w): columns [decay_lo, decay_hi) become the decay
+  // gate -exp(a_log[j]) softplus(v + dt_bias[j]), j = col - decay_lo, and
+  // columns [write_lo, write_hi) the write strength sigmoid(v).
+  int decay_lo, decay_hi, write_lo, write_hi;
+  const float* a_log;
+  const float* dt_bias;
 };
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,

@@ -15,9 +15,11 @@ Pages cited throughout (the extracted text of five web pages on arXiv
 2609.04098, "Why Gated DeltaNet Survives 4-Bit Quantization: NVFP4 W4A4 for
 the Recurrent Half of a Hybrid 27B LLM"):
   [PX]  picx.dev summary page of that title, "Introduction and Theoretical
-        Foundation" > "Background", item 1 (the NVFP4 format).
+        Foundation" > "Background", item 1 (the NVFP4 format), and
+        "Gated DeltaNet Mechanics" (the log-space decay gate).
   [LIT] dmarx anthology record "LIT-800", section "Standing in the anthology"
-        (NVFP4 versus MX block formats; the fused-GEMM mis-scaled gates).
+        (NVFP4 versus MX block formats; the fused-GEMM mis-scaled gates) and
+        "Key takeaways", gates bullet (the sigmoid write strength).
   [CT]  cctest.ai article "Why Gated DeltaNet Holds Up Under 4-Bit
         Quantization", "Main findings", last bullet (global-scale mismatch of
         fused GDN projections, pre-harmonized checkpoint).

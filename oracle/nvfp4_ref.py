@@ -229,6 +229,54 @@ def gemm_segmented_ref(a_codes, a_scales, g_a, w_codes, w_scales, module_gs, mod
     return np.concatenate(ys, axis=1), np.concatenate(ss, axis=1)
 
 
+def softplus(z) -> np.ndarray:
+    """log(1 + e^z) in fp64, as max(z, 0) + log1p(e^-|z|) so that no
+    exponential overflows."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def sigmoid(z) -> np.ndarray:
+    """1 / (1 + e^-z) in fp64, with the exponential taken of -|z| (no overflow)."""
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(-np.abs(z))
+    return np.where(z >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def gdn_decay_gate(v, a_log, dt_bias) -> np.ndarray:
+    """Log-space decay gate of a GDN head: g = -exp(A_log) * softplus(a + dt_bias)
+    ([PX] "Gated DeltaNet Mechanics"); v holds the a-projection outputs
+    [rows, heads], a_log and dt_bias one value per head.  The forget gate is
+    alpha = exp(g), in (0, 1]."""
+    v = np.asarray(v, dtype=np.float64)
+    return -np.exp(np.asarray(a_log, dtype=np.float64)) * softplus(v + np.asarray(dt_bias, dtype=np.float64))
+
+
+def gdn_write_gate(v) -> np.ndarray:
+    """Write strength beta = sigmoid(b) of the b-projection outputs ([LIT]
+    "Key takeaways", gates bullet: the sigmoid write strength)."""
+    return sigmoid(v)
+
+
+def gemm_segmented_gates_ref(a_codes, a_scales, g_a, w_codes, w_scales, module_gs, module_rows,
+                             decay_module, a_log, dt_bias, write_module):
+    """gemm_segmented_ref, then the GDN gates in the epilogue: the columns of
+    module `decay_module` become gdn_decay_gate of their values (column j
+    with a_log[j], dt_bias[j]), those of `write_module` gdn_write_gate; -1
+    selects none.  Returns (G, Y, Sabs): the gated output, and the pre-gate
+    output with its error allowance from gemm_ref."""
+    y, sabs = gemm_segmented_ref(a_codes, a_scales, g_a, w_codes, w_scales, module_gs, module_rows)
+    out = y.copy()
+    starts = np.concatenate([[0], np.cumsum([int(r) for r in module_rows])])
+    if decay_module >= 0:
+        sl = slice(starts[decay_module], starts[decay_module + 1])
+        out[:, sl] = gdn_decay_gate(y[:, sl], a_log, dt_bias)
+    if write_module >= 0:
+        sl = slice(starts[write_module], starts[write_module + 1])
+        out[:, sl] = gdn_write_gate(y[:, sl])
+    return out, y, sabs
+
+
 def harmonize_ref(scales_list, module_gs):
     """Bring per-module tensor scales of a fused projection to one shared scale.
 

@@ -122,6 +122,29 @@ def test_gemm_segmented_rejects_bad_arguments(lib):
     assert lib.nvfp4_last_hip_error() == 0
 
 
+def gg(lib, rows=(8, 4, 2, 2), decay=2, a_log=P16, dt_bias=P16, write=3, M=4, K=32, ldy=16, mgs=P16,
+       host_rows=True):
+    arr = (ctypes.c_int64 * len(rows))(*rows) if host_rows else None
+    return lib.nvfp4_gemm_segmented_gates(P16, P16, P16, P16, P16, mgs, arr, len(rows), decay, a_log, dt_bias,
+                                          write, M, K, P16, 0, ldy, None, 0, None)
+
+
+def test_gemm_segmented_gates_rejects_bad_arguments(lib):
+    assert gg(lib, decay=4) == SHAPE                       # module index out of range
+    assert gg(lib, write=-2) == SHAPE
+    assert gg(lib, decay=3, write=3) == SHAPE              # one module cannot be both gates
+    assert gg(lib, a_log=None) == NULL
+    assert gg(lib, dt_bias=None) == NULL
+    assert gg(lib, a_log=ctypes.c_void_p(0x10002)) == ALIGN
+    assert gg(lib, host_rows=False) == NULL
+    assert gg(lib, ldy=15) == SHAPE                        # ldy < N = 16
+    assert gg(lib, mgs=None) == NULL
+    # no decay gate: its parameters may be NULL; M = 0 enqueues nothing
+    assert gg(lib, decay=-1, a_log=None, dt_bias=None, M=0) == OK
+    assert gg(lib, decay=-1, write=-1, a_log=None, dt_bias=None, M=0) == OK
+    assert lib.nvfp4_last_hip_error() == 0
+
+
 def qg(lib, x=P16, dt=1, ldx=256, a_gs=P16, ptrs=None, M=2, N=64, K=256, y=P16, od=1, ldy=64,
        ws=None, ws_bytes=0):
     p = ptrs or [P16] * 3

@@ -454,3 +454,68 @@ def test_segmented_gemm_special_cases():
     y_seg, s_seg = ref.gemm_segmented_ref(ac, as_, ga, wc, np.concatenate([p[1] for p in parts]), gs, rows)
     y_har, _ = ref.gemm_ref(ac, as_, ga, wc, hs, g_star)
     assert np.all(np.abs(y_seg - y_har) <= 1e-13 * s_seg)
+
+
+# ------------------------------------------------------------------ GDN gates
+def test_softplus_and_sigmoid_closed_forms_and_identities():
+    import math
+    assert abs(ref.softplus(0.0) - math.log(2.0)) < 1e-15
+    z = np.linspace(-30.0, 30.0, 241)
+    # softplus(z) - softplus(-z) = z; sigmoid(z) + sigmoid(-z) = 1
+    assert np.allclose(ref.softplus(z) - ref.softplus(-z), z, rtol=0, atol=1e-12)
+    assert np.allclose(ref.sigmoid(z) + ref.sigmoid(-z), 1.0, rtol=0, atol=1e-15)
+    # sigmoid is the derivative of softplus (central differences)
+    h = 1e-5
+    assert np.allclose((ref.softplus(z + h) - ref.softplus(z - h)) / (2 * h), ref.sigmoid(z), rtol=0, atol=1e-9)
+    assert ref.sigmoid(0.0) == 0.5
+    assert abs(ref.sigmoid(math.log(3.0)) - 0.75) < 1e-15 and abs(ref.sigmoid(-math.log(3.0)) - 0.25) < 1e-15
+    # asymptotes, without overflow
+    with np.errstate(over="raise"):
+        assert abs(ref.softplus(50.0) - 50.0) < 1e-14
+        assert abs(ref.softplus(-50.0) / math.exp(-50.0) - 1.0) < 1e-12
+        assert ref.sigmoid(1000.0) == 1.0 and ref.sigmoid(-1000.0) == 0.0
+
+
+def test_decay_gate_closed_forms():
+    import math
+    dt = np.array([-6.9, -2.25, 0.0, 0.7, 3.0])
+    # at a + dt_bias = 0 the gate is -exp(A_log) ln 2, whatever dt_bias is
+    assert np.allclose(ref.gdn_decay_gate(-dt, np.zeros(5), dt), -math.log(2.0), rtol=0, atol=1e-15)
+    # exp(A_log) multiplies: A_log = ln 2 doubles the gate
+    v = np.array([[-3.0, -0.5, 0.0, 1.5, 9.0]])
+    g0 = ref.gdn_decay_gate(v, np.zeros(5), dt)
+    g1 = ref.gdn_decay_gate(v, np.full(5, math.log(2.0)), dt)
+    assert np.allclose(g1, 2.0 * g0, rtol=1e-15, atol=0)
+    # g <= 0, the forget gate exp(g) lies in (0, 1], and g falls as v grows
+    vs = np.linspace(-20, 20, 81)[:, None]
+    g = ref.gdn_decay_gate(vs, np.full(5, 1.3), dt)
+    assert np.all(g < 0) and np.all(np.exp(g) <= 1.0) and np.all(np.exp(g) > 0)
+    assert np.all(np.diff(g, axis=0) < 0)
+    # far above zero, softplus(z) = z: g = -exp(A_log) (v + dt_bias)
+    big = np.full((1, 5), 60.0)
+    assert np.allclose(ref.gdn_decay_gate(big, np.full(5, 0.5), dt), -math.exp(0.5) * (60.0 + dt), rtol=1e-14)
+    assert np.array_equal(ref.gdn_write_gate(v), ref.sigmoid(v))
+
+
+def test_segmented_gates_are_the_segmented_gemm_then_the_gate_functions():
+    rng = np.random.default_rng(5)
+    rows = [24, 16, 8, 8]
+    K = 64
+    a = ref.quantize(rng.standard_normal((5, K)).astype(np.float32))
+    ws = [ref.quantize((rng.standard_normal((r, K)) * 0.3).astype(np.float32)) for r in rows]
+    wc = np.concatenate([w[0] for w in ws])
+    wsc = np.concatenate([w[1] for w in ws])
+    gs = [w[2] for w in ws]
+    a_log = rng.uniform(0, 2.7, 8)
+    dt_bias = rng.uniform(-6, -2, 8)
+    Y, S = ref.gemm_segmented_ref(*a, wc, wsc, gs, rows)
+    G, Y2, S2 = ref.gemm_segmented_gates_ref(*a, wc, wsc, gs, rows, 2, a_log, dt_bias, 3)
+    assert np.array_equal(Y, Y2) and np.array_equal(S, S2)
+    assert np.array_equal(G[:, :40], Y[:, :40])
+    assert np.array_equal(G[:, 40:48], ref.gdn_decay_gate(Y[:, 40:48], a_log, dt_bias))
+    assert np.array_equal(G[:, 48:], ref.sigmoid(Y[:, 48:]))
+    G0, _, _ = ref.gemm_segmented_gates_ref(*a, wc, wsc, gs, rows, -1, None, None, -1)
+    assert np.array_equal(G0, Y)
+    # the decay module may come first and the write module before it
+    G3, _, _ = ref.gemm_segmented_gates_ref(*a, wc, wsc, gs, rows, 0, rng.uniform(0, 1, 24), np.zeros(24), 1)
+    assert np.all(G3[:, :24] < 0) and np.all((G3[:, 24:40] > 0) & (G3[:, 24:40] < 1))
