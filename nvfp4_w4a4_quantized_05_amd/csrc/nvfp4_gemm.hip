@@ -657,9 +657,52 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     alpha_tab[lane] = col_alpha(g_a, cs, c_first + lane);
     alpha_tab[lane + 64] = col_alpha(g_a, cs, c_first + lane + 64);
   }
-  // kGates: the wave's columns meet a gate range (instantiated only for
-  // GEMMs that have one, so the plain epilogue is unchanged)
-  const bool gated = kGates && cols_gated(cs, c_first, c_last);
+  // kGates (instantiated only for GEMMs that have gate columns): a wave
+  // whose columns meet a gate range takes its own path and leaves; every
+  // other wave takes the strip path below, the same code as without gates.
+  // (A branch on the gate inside the unrolled strip loop made every wave of
+  // a gated GEMM 18% slower.)  The gated path stages acc * alpha in fp32,
+  // 16 rows x 64 columns at a time, in the wave's strip buffer, then applies
+  // the gate functions in a rolled loop over it (one copy of their code) and
+  // stores element by element.  No workgroup barrier follows, so leaving
+  // early is safe.
+  if constexpr (kGates) {
+    static_assert(kStripBytes >= 16 * 64 * 4, "fp32 half strip");
+    if (cols_gated(cs, c_first, c_last)) {
+      float* fs = reinterpret_cast<float*>(smem + STAGES * kStageBytes + wave * kStripBytes);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int hc = 0; hc < 2; ++hc) {
+            if ((r32 >> 4) == sub) {
+#pragma unroll
+              for (int j = 2 * hc; j < 2 * hc + 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                  const int cl = j * 32 + (v >> 2) * 8 + half * 4 + (v & 3);  // column within the wave's 128
+                  fs[(r32 & 15) * 64 + cl - 64 * hc] = acc[j][i][v] * alpha_tab[cl];
+                }
+            }
+            __asm__ volatile("" ::: "memory");  // other lanes' values are read below
+            const int row0 = m0 + wave_m * WM + i * 32 + sub * 16, col0 = c_first + 64 * hc;
+#pragma unroll 1
+            for (int e = lane; e < 16 * 64; e += 64) {
+              const int row = row0 + e / 64, col = col0 + e % 64;
+              if (row < M && col < N) {
+                const float o = col_gate(cs, col, fs[e]);
+                if constexpr (kOutBf16)
+                  reinterpret_cast<__bf16*>(y)[(int64_t)row * ldy + col] = (__bf16)o;
+                else
+                  reinterpret_cast<float*>(y)[(int64_t)row * ldy + col] = o;
+              }
+            }
+            __asm__ volatile("" ::: "memory");  // reads done before the next pass writes
+          }
+      return;
+    }
+  }
   {
     uint8_t* strip = smem + STAGES * kStageBytes + wave * kStripBytes;
     constexpr int kChunksPerRow = WN * kEsz / 16;
@@ -676,23 +719,17 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
             for (int g = 0; g < 4; ++g) {
               const int col = j * 32 + g * 8 + half * 4;
               const floatx4_t al = *reinterpret_cast<const floatx4_t*>(alpha_tab + col);
-              floatx4_t f;
-#pragma unroll
-              for (int t = 0; t < 4; ++t) f[t] = acc[j][i][4 * g + t] * al[t];
-              if constexpr (kGates) {
-                if (gated) {
-#pragma unroll
-                  for (int t = 0; t < 4; ++t) f[t] = col_gate(cs, c_first + col + t, f[t]);
-                }
-              }
               if constexpr (kOutBf16) {
                 typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
                 bf4_t o;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) o[t] = (__bf16)f[t];
+                for (int t = 0; t < 4; ++t) o[t] = (__bf16)(acc[j][i][4 * g + t] * al[t]);
                 *reinterpret_cast<bf4_t*>(rowp + col * kEsz) = o;
               } else {
-                *reinterpret_cast<floatx4_t*>(rowp + col * kEsz) = f;
+                floatx4_t o;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) o[t] = acc[j][i][4 * g + t] * al[t];
+                *reinterpret_cast<floatx4_t*>(rowp + col * kEsz) = o;
               }
             }
         }
