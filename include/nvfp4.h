@@ -193,6 +193,50 @@ NVFP4_API nvfp4_status_t nvfp4_gemm_segmented_gates(const uint8_t* a_codes, cons
                                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nvfp4_gdn_recurrence -- the Gated DeltaNet recurrence of one layer over T
+ * tokens, fp32 state (picx.dev summary page, "Introduction and Theoretical
+ * Foundation" > "Gated DeltaNet Mechanics", the recurrence as printed there):
+ * per value head a state S [128 x 128] (d_k x d_v), and per token t
+ *     S_t = alpha_t S_{t-1} + beta_t khat_t (v_t - S_{t-1}^T khat_t)^T,
+ *     o_t = S_t^T qhat_t / sqrt(128),
+ * with alpha_t = exp(g_t) from the log-space decay gate, beta_t the write
+ * strength, and qhat, khat the L2-normalized q, k of the head (divided by
+ * max(|.|, 1e-6)).  It consumes the projection rows the fused GDN
+ * in-projection writes (nvfp4_gemm_segmented_gates, fp32 output).
+ *
+ *   x           device, [T x ldx] fp32, one row per token (read)
+ *   q_col, k_col   first column of q / k: n_qk_heads heads of 128 values
+ *   v_col       first column of v: n_v_heads heads of 128; -1 reads v as 0
+ *               (the recurrence then carries a state perturbation alone)
+ *   g_col, beta_col   first column of the n_v_heads decay gates g (log of
+ *               alpha) / write strengths beta
+ *   T           tokens, 0 .. INT_MAX (0: nothing is enqueued)
+ *   n_qk_heads, n_v_heads   value head h reads q/k head
+ *               h * n_qk_heads / n_v_heads; n_v_heads % n_qk_heads == 0,
+ *               n_v_heads <= 65535
+ *   state_in    device [n_v_heads x 128 x 128] fp32 (i = d_k row major), or
+ *               NULL for zeros (read)
+ *   state_out   device, same layout, or NULL: S_T (written)
+ *   o           device [T x ldo] fp32, head h at columns 128 h, or NULL
+ *   state_norms device [T x n_v_heads] fp32 or NULL: |S_t|_F^2 per head
+ *   snap_steps, n_snaps, snaps   device: n_snaps strictly increasing token
+ *               indices in [0, T) (int32) and [n_snaps x n_v_heads x 128 x
+ *               128] fp32 out: S_t after those tokens (steps out of order
+ *               are skipped)
+ * Column ranges must lie within ldx (NVFP4_ERR_SHAPE); pointers 4-byte
+ * aligned (NVFP4_ERR_ALIGN).  One workgroup per value head runs the tokens
+ * in order.  Accuracy: the update operator has norm <= 1, so rounding errors
+ * add without growing: |S_t - S_t(exact)|_F <= t (128 + 16) 2^-24 max_s<=t
+ * (|S_s|_F + beta_s |v_s|).
+ */
+NVFP4_API nvfp4_status_t nvfp4_gdn_recurrence(const float* x, int64_t ldx, int64_t q_col, int64_t k_col,
+                                              int64_t v_col, int64_t g_col, int64_t beta_col, int64_t T,
+                                              int32_t n_qk_heads, int32_t n_v_heads, const float* state_in,
+                                              float* state_out, float* o, int64_t ldo, float* state_norms,
+                                              const int32_t* snap_steps, int32_t n_snaps, float* snaps,
+                                              void* stream);
+
+/*
  * nvfp4_quantize_gemm -- quantize the activations with a given (calibrated)
  * tensor scale and multiply: y = nvfp4_gemm(nvfp4_quantize(x, a_gs), W), in
  * one call.  The activation quantization and the linear layer are the ones

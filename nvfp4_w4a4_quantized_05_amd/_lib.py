@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NV
                 4: "NVFP4_ERR_MODE", 5: "NVFP4_ERR_ALIGN", 6: "NVFP4_ERR_WORKSPACE",
                 7: "NVFP4_ERR_HIP", 8: "NVFP4_ERR_ALIAS"}
 EXPORTS = ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_segmented", "nvfp4_gemm_segmented_gates",
-           "nvfp4_quantize_gemm",
+           "nvfp4_quantize_gemm", "nvfp4_gdn_recurrence",
            "nvfp4_quantize_gemm_workspace_size", "nvfp4_harmonize_fused_scales",
            "nvfp4_gemm_workspace_size", "nvfp4_status_string", "nvfp4_last_hip_error")
 
@@ -59,6 +59,9 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_gemm_segmented_gates.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(i64), i32, i32, vp, vp, i32,
                                                i64, i64, vp, i32, i64, vp, sz, vp]
     lib.nvfp4_gemm_segmented_gates.restype = i32
+    lib.nvfp4_gdn_recurrence.argtypes = [vp, i64, i64, i64, i64, i64, i64, i64, i32, i32, vp, vp, vp, i64, vp, vp,
+                                         i32, vp, vp]
+    lib.nvfp4_gdn_recurrence.restype = i32
     lib.nvfp4_quantize_gemm.argtypes = [vp, i32, i64, vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp, sz, vp]
     lib.nvfp4_quantize_gemm.restype = i32
     lib.nvfp4_quantize_gemm_workspace_size.argtypes = [i64, i64, i64, i32, i32]
@@ -226,6 +229,42 @@ def gemm_segmented_gates(a_codes, a_scales, a_gs, w_codes, w_scales, module_gs, 
                                         out.stride(0), _ptr(ws), ws_bytes, _stream(stream))
     _check(st, "nvfp4_gemm_segmented_gates")
     return out
+
+
+def gdn_recurrence(x: torch.Tensor, *, q_col: int, k_col: int, v_col: int, g_col: int, beta_col: int,
+                   n_qk_heads: int, n_v_heads: int, state_in: torch.Tensor | None = None,
+                   state_out: torch.Tensor | None = None, o: torch.Tensor | None = None,
+                   state_norms: torch.Tensor | None = None, snap_steps: torch.Tensor | None = None,
+                   snaps: torch.Tensor | None = None, stream=None):
+    """Gated DeltaNet recurrence over the T rows of x (fp32 [T, ldx]: q, k,
+    v, g, beta at the given columns; v_col = -1 reads v as zero).  Writes
+    whichever of state_out [Hv,128,128], o [T, >= Hv*128], state_norms
+    [T, Hv] and snaps [n, Hv, 128, 128] (at int32 snap_steps) are given."""
+    _need_gpu(x, state_in, state_out, o, state_norms, snap_steps, snaps)
+    if x.dim() != 2 or x.dtype != torch.float32 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D float32 tensor with unit column stride")
+    T = x.shape[0]
+    st_shape = (n_v_heads, 128, 128)
+    for t in (state_in, state_out):
+        if t is not None and (t.shape != st_shape or t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("states must be contiguous float32 [n_v_heads, 128, 128]")
+    if o is not None and (o.dtype != torch.float32 or o.dim() != 2 or o.shape[0] != T or o.stride(1) != 1):
+        raise ValueError("o must be float32 [T, >= n_v_heads*128] with unit column stride")
+    if state_norms is not None and (state_norms.shape != (T, n_v_heads) or state_norms.dtype != torch.float32
+                                    or not state_norms.is_contiguous()):
+        raise ValueError("state_norms must be contiguous float32 [T, n_v_heads]")
+    n_snaps = 0
+    if snap_steps is not None:
+        n_snaps = snap_steps.numel()
+        if snap_steps.dtype != torch.int32 or snaps is None or snaps.shape != (n_snaps, *st_shape) \
+                or snaps.dtype != torch.float32 or not snaps.is_contiguous():
+            raise ValueError("snap_steps int32 [n] with snaps float32 [n, n_v_heads, 128, 128]")
+    st = load().nvfp4_gdn_recurrence(_ptr(x), x.stride(0), q_col, k_col, v_col, g_col, beta_col, T, n_qk_heads,
+                                     n_v_heads, _ptr(state_in), _ptr(state_out), _ptr(o),
+                                     o.stride(0) if o is not None else 0, _ptr(state_norms),
+                                     _ptr(snap_steps), n_snaps, _ptr(snaps), _stream(stream))
+    _check(st, "nvfp4_gdn_recurrence")
+    return state_out
 
 
 def quantize_gemm(x: torch.Tensor, a_gs: torch.Tensor, w_codes, w_scales, w_gs, *, out_dtype=torch.float32,

@@ -148,6 +148,35 @@ nvfp4_status_t nvfp4_gemm_segmented_gates(const uint8_t* a_codes, const uint8_t*
   }
 }
 
+nvfp4_status_t nvfp4_gdn_recurrence(const float* x, int64_t ldx, int64_t q_col, int64_t k_col, int64_t v_col,
+                                    int64_t g_col, int64_t beta_col, int64_t T, int32_t n_qk_heads,
+                                    int32_t n_v_heads, const float* state_in, float* state_out, float* o,
+                                    int64_t ldo, float* state_norms, const int32_t* snap_steps, int32_t n_snaps,
+                                    float* snaps, void* stream) {
+  try {
+    constexpr int64_t kD = 128;
+    if (T < 0 || T > INT_MAX || ldx <= 0 || ldx > INT_MAX) return NVFP4_ERR_SHAPE;
+    if (n_qk_heads < 1 || n_v_heads < 1 || n_v_heads > 65535 || n_v_heads % n_qk_heads != 0) return NVFP4_ERR_SHAPE;
+    if (q_col < 0 || q_col + n_qk_heads * kD > ldx || k_col < 0 || k_col + n_qk_heads * kD > ldx)
+      return NVFP4_ERR_SHAPE;
+    if (v_col < -1 || (v_col >= 0 && v_col + n_v_heads * kD > ldx)) return NVFP4_ERR_SHAPE;
+    if (g_col < 0 || g_col + n_v_heads > ldx || beta_col < 0 || beta_col + n_v_heads > ldx) return NVFP4_ERR_SHAPE;
+    if (o && ldo < n_v_heads * kD) return NVFP4_ERR_SHAPE;
+    if (n_snaps < 0) return NVFP4_ERR_SHAPE;
+    if (T == 0) return NVFP4_OK;
+    if (!x || (n_snaps > 0 && (!snap_steps || !snaps))) return NVFP4_ERR_NULL;
+    for (const void* p : {(const void*)x, (const void*)state_in, (const void*)state_out, (const void*)o,
+                          (const void*)state_norms, (const void*)snap_steps, (const void*)snaps})
+      if (p && !aligned(p, 4)) return NVFP4_ERR_ALIGN;
+    return hip_status(nvfp4::launch_gdn_recurrence(x, ldx, q_col, k_col, v_col, g_col, beta_col, T, n_qk_heads,
+                                                   n_v_heads, state_in, state_out, o, ldo, state_norms,
+                                                   snap_steps, n_snaps > 0 ? n_snaps : 0, snaps,
+                                                   (hipStream_t)stream));
+  } catch (...) {
+    return NVFP4_ERR_HIP;
+  }
+}
+
 size_t nvfp4_quantize_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t in_dtype, int32_t out_dtype) {
   (void)out_dtype;
   if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0 || M > INT_MAX || K > INT_MAX) return 0;

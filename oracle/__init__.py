@@ -10,6 +10,8 @@ Modules:
               fused-scale harmonization, naive fused GEMM)
   exact       exact-rational twin written with ``fractions.Fraction`` for
               brute-force checks of ``nvfp4_ref`` on small inputs
+  gdn_ref     the Gated DeltaNet recurrence, token by token in fp64 (the
+              second workload: quantized projections feeding the state)
 
 Pages cited throughout (the extracted text of five web pages on arXiv
 2609.04098, "Why Gated DeltaNet Survives 4-Bit Quantization: NVFP4 W4A4 for

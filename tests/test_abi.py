@@ -205,3 +205,27 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 32, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         _lib.quantize(x)
+
+
+def gd(lib, x=P16, ldx=1040, cols=(0, 256, 512, 1024, 1028), T=8, nqk=2, nv_=4, o=None, ldo=0, n_snaps=0,
+       steps=None, snaps=None, s_in=None):
+    return lib.nvfp4_gdn_recurrence(x, ldx, *cols, T, nqk, nv_, s_in, None, o, ldo, None, steps, n_snaps, snaps,
+                                    None)
+
+
+def test_gdn_recurrence_rejects_bad_arguments(lib):
+    assert gd(lib, T=-1) == SHAPE
+    assert gd(lib, nqk=3) == SHAPE                          # 4 value heads not a multiple of 3
+    assert gd(lib, nv_=0) == SHAPE
+    assert gd(lib, cols=(0, 256, 512, 1024, 1037)) == SHAPE  # beta columns past ldx
+    assert gd(lib, cols=(0, 900, 512, 1024, 1028)) == SHAPE  # k columns past ldx
+    assert gd(lib, cols=(0, 256, -2, 1024, 1028)) == SHAPE
+    assert gd(lib, o=P16, ldo=511) == SHAPE                  # ldo < 4 * 128
+    assert gd(lib, n_snaps=-1) == SHAPE
+    assert gd(lib, x=None) == NULL
+    assert gd(lib, n_snaps=2, steps=None, snaps=P16) == NULL
+    assert gd(lib, x=ctypes.c_void_p(0x10002)) == ALIGN
+    assert gd(lib, s_in=ctypes.c_void_p(0x10002)) == ALIGN
+    assert gd(lib, T=0, x=None) == OK                        # nothing to do
+    assert gd(lib, T=0, cols=(0, 256, -1, 1024, 1028)) == OK  # v = 0 is allowed
+    assert lib.nvfp4_last_hip_error() == 0

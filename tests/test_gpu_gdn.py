@@ -1,0 +1,109 @@
+"""nvfp4_gdn_recurrence against the fp64 recurrence reference.
+
+Tolerance (from the arithmetic, as the header states): the update operator
+has norm <= 1, so per-token fp32 rounding adds up without growing:
+|S_t - S_t(ref)|_F <= t (128 + 16) 2^-24 M_t with M_t = max over s <= t of
+|S_s|_F + beta_s |v_s|.  An output o_t = S_t^T qhat / sqrt(128) then differs
+by at most (that bound + 128 2^-24 |S_t|_F) / sqrt(128)."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_w4a4_quantized_05_amd as nv
+from oracle import gdn_ref as G
+from tests.gpu_util import need_gpu
+
+pytestmark = pytest.mark.gpu
+D = 128
+LAYOUT = dict(q_col=0, k_col=2 * D, v_col=4 * D, g_col=8 * D, beta_col=8 * D + 4)  # n_qk 2, n_v 4
+LDX = 8 * D + 16
+
+
+def _rows(T, seed, v_zero=False):
+    """Projection rows: q, k, v ~ N(0, 1); g = -exp(A_log) softplus(a + dt_bias)
+    with A = U(1, 16), dt_bias for dt in [1e-3, 0.1], a ~ N(0, 1); beta = sigmoid(N(0, 1))."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((T, LDX), np.float32)
+    x[:, :8 * D] = rng.standard_normal((T, 8 * D))
+    if v_zero:
+        x[:, 4 * D:8 * D] = 0
+    a_log = np.log(rng.uniform(1, 16, 4))
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), 4))
+    dt_bias = dt + np.log(-np.expm1(-dt))
+    z = rng.standard_normal((T, 4)) + dt_bias
+    x[:, 8 * D:8 * D + 4] = -np.exp(a_log) * (np.maximum(z, 0) + np.log1p(np.exp(-np.abs(z))))
+    x[:, 8 * D + 4:8 * D + 8] = 1 / (1 + np.exp(-rng.standard_normal((T, 4))))
+    return x
+
+
+def _check(x, s0=None, snaps=(), v_col=4 * D):
+    dev = need_gpu()
+    T = x.shape[0]
+    lay = dict(LAYOUT, v_col=v_col)
+    xt = torch.from_numpy(x).to(dev)
+    so = torch.empty((4, D, D), dtype=torch.float32, device=dev)
+    o = torch.full((T, 4 * D + 32), np.nan, dtype=torch.float32, device=dev)   # ldo > 4 D
+    nr = torch.empty((T, 4), dtype=torch.float32, device=dev)
+    st = torch.tensor(list(snaps), dtype=torch.int32, device=dev) if snaps else None
+    sn = torch.empty((len(snaps), 4, D, D), dtype=torch.float32, device=dev) if snaps else None
+    nv.gdn_recurrence(xt, **lay, n_qk_heads=2, n_v_heads=4,
+                      state_in=None if s0 is None else torch.from_numpy(s0.astype(np.float32)).to(dev),
+                      state_out=so, o=o, state_norms=nr, snap_steps=st, snaps=sn)
+    torch.cuda.synchronize()
+    q, k, v, g, beta = G.split_projection_rows(x, **lay, n_qk=2, n_v=4)
+    O, S, SN, NR = G.gdn_recurrence_ref(q, k, v, g, beta, s0=s0, snap_steps=snaps)
+    # running bound M_t per head and the per-token error allowance
+    norm_S = np.sqrt(NR)                                         # [T, heads]
+    drive = beta * np.linalg.norm(v, axis=2)
+    M = np.maximum.accumulate(norm_S + drive, axis=0)
+    if s0 is not None:
+        M = np.maximum(M, np.linalg.norm(s0.reshape(4, -1), axis=1)[None, :])
+    steps = np.arange(1, T + 1)[:, None]
+    e_S = steps * (D + 16) * 2.0 ** -24 * M                      # [T, heads]
+    # final state
+    err = np.linalg.norm((so.cpu().numpy() - S).reshape(4, -1), axis=1)
+    assert np.all(err <= e_S[-1]), f"state error {err} > {e_S[-1]}"
+    # outputs, per token and head
+    ov = o.cpu().numpy()
+    assert np.all(np.isnan(ov[:, 4 * D:])), "o written past its columns"
+    oe = np.linalg.norm(ov[:, :4 * D].reshape(T, 4, D) - O, axis=2)
+    o_tol = (e_S + D * 2.0 ** -24 * norm_S) / np.sqrt(D)
+    assert np.all(oe <= o_tol), f"output error {oe.max()} (worst ratio {np.max(oe / o_tol):.3f})"
+    # norms and snapshots
+    assert np.all(np.abs(np.sqrt(nr.cpu().numpy()) - norm_S) <= e_S + 1e-30)
+    for i, s in enumerate(snaps):
+        se = np.linalg.norm((sn[i].cpu().numpy() - SN[i]).reshape(4, -1), axis=1)
+        assert np.all(se <= e_S[s]), f"snapshot {s}: {se} > {e_S[s]}"
+    return float(np.max(err / e_S[-1]))
+
+
+def test_recurrence_short_with_snapshots():
+    print("[gdn] T=300 snapshots", flush=True)
+    _check(_rows(300, 1), snaps=(0, 1, 77, 150, 299))
+
+
+def test_recurrence_from_a_start_state():
+    print("[gdn] T=257 start state", flush=True)
+    rng = np.random.default_rng(7)
+    _check(_rows(257, 2), s0=rng.standard_normal((4, D, D)) * 0.05, snaps=(3, 256))
+
+
+def test_recurrence_carries_a_perturbation_with_zero_v():
+    # v_col = -1: the state is a perturbation; it decays by the same operator
+    print("[gdn] T=200 v = 0, impulse", flush=True)
+    rng = np.random.default_rng(8)
+    x = _rows(200, 3, v_zero=True)
+    _check(x, s0=rng.standard_normal((4, D, D)) * 0.01, v_col=-1)
+
+
+def test_recurrence_long():
+    print("[gdn] T=3000", flush=True)
+    _check(_rows(3000, 4), snaps=(999, 2999))
+
+
+def test_single_token_and_empty():
+    print("[gdn] T=1 and T=0", flush=True)
+    _check(_rows(1, 5), snaps=(0,))
+    dev = need_gpu()
+    nv.gdn_recurrence(torch.zeros((0, LDX), dtype=torch.float32, device=dev), **LAYOUT, n_qk_heads=2, n_v_heads=4)
+    torch.cuda.synchronize()
