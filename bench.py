@@ -228,6 +228,8 @@ def main():
     if not args.no_extras:
         extra["gate_error_compression"] = gate_error_compression(nv, torch, np, dev, xs[0], calib[0], wq, w_gates,
                                                                  seed)
+        extra["mlp_swiglu_quantize_epilogue"] = mlp_fused(nv, torch, np, dev, stream, xs, calib, qbuf, wq, gemms,
+                                                          ys, T, args.steps)
         extra["gdn_recurrence_lockstep"] = gdn_lockstep(nv, torch, np, dev, xs[0], calib[0], in_codes,
                                                         in_scales_modules, module_gs, [P[n].n for n in fused],
                                                         w_fp32, seed)
@@ -356,6 +358,73 @@ def extra_measurements(nv, torch, np, dev, stream, xs, calib, qbuf, ys, in_codes
         qg[str(m)] = res
     out["decode_quantize_gemm_in_proj_12384x5120"] = qg
     del copies, hcopies
+    return out
+
+
+def mlp_fused(nv, torch, np, dev, stream, xs, calib, qbuf, wq, gemms, ys, T, steps):
+    """The MLP with SwiGLU between gate/up and down (an assumption: the pages
+    do not describe the activation), with the quantization of the down
+    projection's input done in the gate/up GEMM's epilogue
+    (nvfp4_gemm_swiglu_quantize), so that the gate/up output never goes to
+    memory in bf16.  Reported: that kernel against the two kernels of the
+    step it stands in for (gate/up GEMM with bf16 output, then the quantize
+    of X_d; the step has no SwiGLU pass, so the comparison favours the
+    unfused side), and the whole layer step with the fused MLP (down GEMM on
+    the fused codes; same GEMM flops as `value`)."""
+    qa = qbuf[2]
+    wc, wsc, wg = wq["gate_up"]
+    F = wc.shape[0] // 2
+    h = torch.empty((T, F), dtype=torch.float32, device=dev)
+    nv.gemm_swiglu_quantize(qa[0], qa[1], calib[2], wc, wsc, wg, torch.ones(1, device=dev), h=h)
+    h_gs = nv.quantize(h)[2].clone()          # static scale of h, calibrated once (amax mode)
+    del h
+    hc = torch.empty((T, F // 2), dtype=torch.uint8, device=dev)
+    hs = torch.empty((T, F // 16), dtype=torch.uint8, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def unfused():
+        nv.gemm(qa[0], qa[1], calib[2], wc, wsc, wg, out_dtype=torch.bfloat16, out=ys[2])
+        nv.quantize(xs[3], calib[3], from_amax=False, codes=qbuf[3][0], scales=qbuf[3][1])
+
+    def fused():
+        nv.gemm_swiglu_quantize(qa[0], qa[1], calib[2], wc, wsc, wg, h_gs, codes=hc, scales=hs)
+
+    best = {"gate_up_gemm_plus_quantize_ms": float("inf"), "fused_ms": float("inf")}
+    for _ in range(3):
+        for label, fn in (("gate_up_gemm_plus_quantize_ms", unfused), ("fused_ms", fused)):
+            fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(3):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best[label] = min(best[label], e0.elapsed_time(e1) / 3)
+
+    # the layer step with the fused MLP
+    def step_fused():
+        for gi, (name, xi, gwc, gws, gwg, n, k) in enumerate(gemms):
+            if name == "gate_up":
+                fused()
+            elif name == "down":
+                nv.gemm(hc, hs, h_gs, gwc, gws, gwg, out_dtype=torch.bfloat16, out=ys[gi])
+            else:
+                nv.quantize(xs[xi], calib[xi], from_amax=False, codes=qbuf[xi][0], scales=qbuf[xi][1])
+                nv.gemm(qbuf[xi][0], qbuf[xi][1], calib[xi], gwc, gws, gwg, out_dtype=torch.bfloat16, out=ys[gi])
+    step_fused()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step_fused()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = sum(2.0 * T * g[5] * g[6] for g in gemms)
+    out = {k: round(v, 4) for k, v in best.items()}
+    out["bytes_saved_per_call_gb"] = round((T * 2 * F * 2 + T * F * 2) / 1e9, 3)
+    out["layer_step_ms"] = round(ms, 4)
+    out["layer_step_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+    del hc, hs
     return out
 
 

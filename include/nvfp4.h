@@ -193,6 +193,41 @@ NVFP4_API nvfp4_status_t nvfp4_gemm_segmented_gates(const uint8_t* a_codes, cons
                                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nvfp4_gemm_swiglu_quantize -- the MLP gate/up projection with its output
+ * quantized for the down projection in the GEMM's epilogue, so that the
+ * gate/up output never goes to memory in bf16.  The pages quantize every
+ * linear layer's activations to NVFP4 (picx.dev summary page, "Background",
+ * item 1; dmarx anthology record LIT-800, "Key takeaways", recipe bullet);
+ * the SwiGLU between the two projections is not on the pages and is this
+ * call's assumption: with W = [gate (F rows); up (F rows)] x K,
+ *     v = RN32(g_a g_w) deq(A) deq(W)^T          (as nvfp4_gemm, fp32)
+ *     h = silu(v_gate) v_up,  silu(x) = x / (1 + exp(-x))
+ * in fp32, silu with the hardware exp2 of -x log2(e) and reciprocal
+ * and h [M x F] is quantized with the given tensor scale exactly as
+ * nvfp4_quantize (GIVEN mode) quantizes fp32 input: the same bytes.
+ *
+ *   a_codes, a_scales, a_gs   as for nvfp4_gemm (A = [M x K])
+ *   w_codes, w_scales, w_gs   the gate and up weights concatenated along N
+ *                             ([2F x K], one tensor scale)
+ *   M, F, K        M >= 0; F > 0, F % 64 == 0; K > 0, K % 128 == 0;
+ *                  M * K / 2 and 2 F * K / 2 below 2^31
+ *   h_gs           device, one float: h's tensor scale (read; calibrated)
+ *   h_codes, h_scales  device out, [M x F/2] and [M x F/16]
+ *   h, ldh         device out [M x ldh] fp32 (ldh >= F, ldh % 4 == 0,
+ *                  16-byte aligned), or NULL: h itself
+ * Only the streaming kernel has this epilogue; codes and scales of A and W
+ * must be 16- and 8-byte aligned (NVFP4_ERR_ALIGN), h_codes 8-byte.
+ * Accuracy: v as nvfp4_gemm; h is silu(v_gate) v_up to a few fp32 ulp plus
+ * |v_gate| 2^-23 relative (the rounding of v_gate log2(e)); the quantization
+ * is exact for that fp32 h.
+ */
+NVFP4_API nvfp4_status_t nvfp4_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_scales,
+                                                    const float* a_gs, const uint8_t* w_codes,
+                                                    const uint8_t* w_scales, const float* w_gs, int64_t M,
+                                                    int64_t F, int64_t K, const float* h_gs, uint8_t* h_codes,
+                                                    uint8_t* h_scales, float* h, int64_t ldh, void* stream);
+
+/*
  * nvfp4_gdn_recurrence -- the Gated DeltaNet recurrence of one layer over T
  * tokens, fp32 state (picx.dev summary page, "Introduction and Theoretical
  * Foundation" > "Gated DeltaNet Mechanics", the recurrence as printed there):

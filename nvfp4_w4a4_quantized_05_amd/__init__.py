@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     gemm,
     gemm_segmented,
     gemm_segmented_gates,
+    gemm_swiglu_quantize,
     gdn_recurrence,
     harmonize_fused_scales,
     load,

@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NV
                 4: "NVFP4_ERR_MODE", 5: "NVFP4_ERR_ALIGN", 6: "NVFP4_ERR_WORKSPACE",
                 7: "NVFP4_ERR_HIP", 8: "NVFP4_ERR_ALIAS"}
 EXPORTS = ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_segmented", "nvfp4_gemm_segmented_gates",
-           "nvfp4_quantize_gemm", "nvfp4_gdn_recurrence",
+           "nvfp4_quantize_gemm", "nvfp4_gdn_recurrence", "nvfp4_gemm_swiglu_quantize",
            "nvfp4_quantize_gemm_workspace_size", "nvfp4_harmonize_fused_scales",
            "nvfp4_gemm_workspace_size", "nvfp4_status_string", "nvfp4_last_hip_error")
 
@@ -59,6 +59,8 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_gemm_segmented_gates.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(i64), i32, i32, vp, vp, i32,
                                                i64, i64, vp, i32, i64, vp, sz, vp]
     lib.nvfp4_gemm_segmented_gates.restype = i32
+    lib.nvfp4_gemm_swiglu_quantize.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, i64, vp]
+    lib.nvfp4_gemm_swiglu_quantize.restype = i32
     lib.nvfp4_gdn_recurrence.argtypes = [vp, i64, i64, i64, i64, i64, i64, i64, i32, i32, vp, vp, vp, i64, vp, vp,
                                          i32, vp, vp]
     lib.nvfp4_gdn_recurrence.restype = i32
@@ -229,6 +231,37 @@ def gemm_segmented_gates(a_codes, a_scales, a_gs, w_codes, w_scales, module_gs, 
                                         out.stride(0), _ptr(ws), ws_bytes, _stream(stream))
     _check(st, "nvfp4_gemm_segmented_gates")
     return out
+
+
+def gemm_swiglu_quantize(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, h_gs, *, codes=None, scales=None,
+                         h: torch.Tensor | None = None, stream=None):
+    """h = silu(gate) * up of the gate/up GEMM (W = [gate; up], 2F rows),
+    quantized with tensor scale h_gs in the epilogue.  Returns (codes
+    [M, F/2], scales [M, F/16], h_gs); h [M, >= F] fp32 is filled if given."""
+    _need_gpu(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, h_gs, codes, scales, h)
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    if w_codes.shape[0] % 2 or w_codes.shape[1] * 2 != K or a_scales.shape != (M, K // 16) \
+            or w_scales.shape != (w_codes.shape[0], K // 16):
+        raise ValueError("operand shapes disagree")
+    F = w_codes.shape[0] // 2
+    for t in (a_codes, a_scales, w_codes, w_scales):
+        if not t.is_contiguous() or t.dtype != torch.uint8:
+            raise ValueError("codes and scales must be contiguous uint8")
+    if codes is None:
+        codes = torch.empty((M, F // 2), dtype=torch.uint8, device=a_codes.device)
+    if scales is None:
+        scales = torch.empty((M, F // 16), dtype=torch.uint8, device=a_codes.device)
+    if codes.shape != (M, F // 2) or scales.shape != (M, F // 16) or not codes.is_contiguous() \
+            or not scales.is_contiguous():
+        raise ValueError("codes [M, F/2] and scales [M, F/16], contiguous")
+    if h is not None and (h.dtype != torch.float32 or h.dim() != 2 or h.shape[0] != M or h.stride(1) != 1):
+        raise ValueError("h must be float32 [M, >= F] with unit column stride")
+    st = load().nvfp4_gemm_swiglu_quantize(_ptr(a_codes), _ptr(a_scales), _ptr(a_gs), _ptr(w_codes),
+                                           _ptr(w_scales), _ptr(w_gs), M, F, K, _ptr(h_gs), _ptr(codes),
+                                           _ptr(scales), _ptr(h), h.stride(0) if h is not None else 0,
+                                           _stream(stream))
+    _check(st, "nvfp4_gemm_swiglu_quantize")
+    return codes, scales, h_gs
 
 
 def gdn_recurrence(x: torch.Tensor, *, q_col: int, k_col: int, v_col: int, g_col: int, beta_col: int,

@@ -177,6 +177,32 @@ nvfp4_status_t nvfp4_gdn_recurrence(const float* x, int64_t ldx, int64_t q_col, 
   }
 }
 
+nvfp4_status_t nvfp4_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                                          const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
+                                          int64_t M, int64_t F, int64_t K, const float* h_gs, uint8_t* h_codes,
+                                          uint8_t* h_scales, float* h, int64_t ldh, void* stream) {
+  try {
+    if (M < 0 || F <= 0 || K <= 0 || K % 128 != 0 || F % 64 != 0) return NVFP4_ERR_SHAPE;
+    if (M > INT_MAX || F > INT_MAX / 2 || K > INT_MAX) return NVFP4_ERR_SHAPE;
+    if (h && ldh < F) return NVFP4_ERR_SHAPE;
+    // 32-bit buffer offsets of the streaming kernel
+    if (M * (K / 2) >= ((int64_t)1 << 31) || 2 * F * (K / 2) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+    if (M == 0) return NVFP4_OK;
+    if (!a_codes || !a_scales || !a_gs || !w_codes || !w_scales || !w_gs || !h_gs || !h_codes || !h_scales)
+      return NVFP4_ERR_NULL;
+    if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_scales, 8) || !aligned(w_scales, 8) ||
+        !aligned(a_gs, 4) || !aligned(w_gs, 4) || !aligned(h_gs, 4) || !aligned(h_codes, 8) ||
+        (h && (!aligned(h, 16) || ldh % 4 != 0)))
+      return NVFP4_ERR_ALIGN;
+    if (((M + 255) / 256) * ((2 * F + 255) / 256) > (int64_t)INT_MAX) return NVFP4_ERR_SHAPE;
+    nvfp4::SwigluOut out{h_gs, h_codes, h_scales, h, ldh, (int)F};
+    return hip_status(nvfp4::launch_gemm_swiglu_quantize(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, M, F, K,
+                                                         out, (hipStream_t)stream));
+  } catch (...) {
+    return NVFP4_ERR_HIP;
+  }
+}
+
 size_t nvfp4_quantize_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t in_dtype, int32_t out_dtype) {
   (void)out_dtype;
   if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0 || M > INT_MAX || K > INT_MAX) return 0;

@@ -108,6 +108,14 @@ __device__ __forceinline__ float col_alpha(float g_a, const ColScales& cs, int c
   return g_a * cs.gs[col_range(cs, col)];
 }
 
+// silu(x) = x / (1 + e^-x) with the hardware exp2 of -x log2(e) and the
+// hardware reciprocal: a few ulp, plus |x| 2^-23 relative from rounding
+// x log2(e).  Large negative x gives 1 / inf = 0 (silu -> -0), large
+// positive x gives x.
+__device__ __forceinline__ float silu_fast(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+
 // Whether output columns [c0, c1] meet a gate column range.
 __device__ __forceinline__ bool cols_gated(const ColScales& cs, int c0, int c1) {
   return (c0 < cs.decay_hi && c1 >= cs.decay_lo) || (c0 < cs.write_hi && c1 >= cs.write_lo);
@@ -403,11 +411,11 @@ __device__ __forceinline__ int chunk_swizzle(int row) { return ((row >> 1) ^ (ro
 //   accumulators hold 4 consecutive output columns of one row: the epilogue
 //   stages rows in LDS with 8-byte writes and stores 16-byte row chunks.
 // Rows past M or N read a clamped (valid) row; their outputs are never stored.
-template <int STAGES, bool kOutBf16, bool kGates>
+template <int STAGES, bool kOutBf16, bool kGates, bool kSwiglu>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const ColScales cs,
-    int M, int N, int K, void* __restrict__ y, int64_t ldy) {
+    int M, int N, int K, void* __restrict__ y, int64_t ldy, const SwigluOut sw) {
   constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FM = 4, FN = 4;
   constexpr int kCodeBytes = BM * kRowBytes;          // 16 KiB per operand per stage
   constexpr int kStageScaleBytes = BM * kScaleBytes;  // 2 KiB per operand per stage
@@ -444,19 +452,34 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_scales, (int64_t)M * srow_bytes);
   const __amdgpu_buffer_rsrc_t rws = make_rsrc(w_scales, (int64_t)N * srow_bytes);
   uint32_t a_off[4], w_off[4], as_off[2], ws_off[2];
+  // W row of tile row r.  kSwiglu: the tile's 256 rows are gate and up rows
+  // of its 128 output columns c0 = n0 / 2 .. + 127, in blocks of 32: wave
+  // half wn = r / 128 covers columns c0 + 64 wn + 32 b + e (b = (r / 64) % 2,
+  // e = r % 32), rows 32 b .. of the half being gate (r / 32 even) or up
+  // (odd).  So a lane's accumulator blocks j = 0, 2 (gate) and 1, 3 (up) hold
+  // the same output elements.  Rows past F repeat row F - 1 (outputs past F
+  // are not written).
+  auto w_row = [&](int n0, int r) -> int {
+    if constexpr (kSwiglu) {
+      const int col = n0 / 2 + 64 * (r >> 7) + 32 * ((r >> 6) & 1) + (r & 31);
+      return min(col, sw.F - 1) + (((r >> 5) & 1) ? sw.F : 0);
+    } else {
+      return min(n0 + r, N - 1);
+    }
+  };
   auto set_sources = [&](int m0, int n0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wave * 64 + 16 * i + (lane >> 2);
       const int chunk = (lane & 3) ^ chunk_swizzle(row);
       a_off[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)row_bytes + chunk * 16;
-      w_off[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)row_bytes + chunk * 16;
+      w_off[i] = (uint32_t)w_row(n0, row) * (uint32_t)row_bytes + chunk * 16;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = wave * 64 + 32 * i + (lane >> 1);
       as_off[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)srow_bytes + (lane & 1) * 4;
-      ws_off[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)srow_bytes + (lane & 1) * 4;
+      ws_off[i] = (uint32_t)w_row(n0, row) * (uint32_t)srow_bytes + (lane & 1) * 4;
     }
   };
   auto issue_stage = [&](int ks, int slot) {
@@ -646,6 +669,60 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   // covers all 128 columns (every plain GEMM, and most tiles of a segmented
   // one) the table holds one value, found with one lookup.
   const float g_a = *a_gs;
+  if constexpr (kSwiglu) {
+    // h = silu(g) u of the wave's 64 output columns c_out .. + 63 (v = acc
+    // RN32(g_a g_w) for both), staged in fp32 in the wave's strip buffer, 16
+    // rows at a time: 16 x 64 values, i.e. 64 blocks of 16, one per lane.
+    // Each lane then quantizes its block with the quantize kernel's
+    // arithmetic and stores 8 code bytes and 1 scale byte (and, if asked,
+    // the 16 fp32 values).
+    static_assert(kStripBytes >= 16 * 64 * 4, "fp32 strip of 16 x 64");
+    const float alpha = g_a * cs.gs[0];
+    const int c_out = n0 / 2 + 64 * wave_n;
+    float* fs = reinterpret_cast<float*>(smem + STAGES * kStageBytes + wave * kStripBytes);
+    const float hg = *sw.gs, r6 = __builtin_amdgcn_rcpf(6.0f * hg);
+    const int qr = lane >> 2, qb = lane & 3;  // the lane's block: strip row, 16-column block
+    if (c_out < sw.F) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          if ((r32 >> 4) == sub) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                const float gv = acc[2 * jj][i][v] * alpha, uv = acc[2 * jj + 1][i][v] * alpha;
+                fs[(r32 & 15) * 64 + 32 * jj + (v >> 2) * 8 + half * 4 + (v & 3)] = silu_fast(gv) * uv;
+              }
+          }
+          __asm__ volatile("" ::: "memory");  // other lanes' values are read below
+          const int row = m0 + wave_m * WM + i * 32 + sub * 16 + qr;
+          const floatx4_t* src = reinterpret_cast<const floatx4_t*>(fs + qr * 64 + 16 * qb);
+          float vals[16];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const floatx4_t f4 = src[e];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) vals[4 * e + t] = f4[t];
+          }
+          __asm__ volatile("" ::: "memory");  // reads done before the next strip is written
+          if (row < M) {
+            uint32_t w0, w1;
+            const uint32_t sc = quantize_block(vals, hg, r6, w0, w1);
+            const int col = c_out + 16 * qb;
+            *reinterpret_cast<u32x2_t*>(sw.codes + (int64_t)row * (sw.F / 2) + col / 2) = u32x2_t{w0, w1};
+            sw.scales[(int64_t)row * (sw.F / 16) + col / 16] = (uint8_t)sc;
+            if (sw.h) {
+              floatx4_t* dst = reinterpret_cast<floatx4_t*>(sw.h + (int64_t)row * sw.ldh + col);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) dst[e] = floatx4_t{vals[4 * e], vals[4 * e + 1], vals[4 * e + 2], vals[4 * e + 3]};
+            }
+          }
+        }
+    }
+    return;
+  }
   const int c_first = n0 + wave_n * WN, c_last = min(c_first + WN, N) - 1;
   const int s_first = col_range(cs, c_first);
   float* const alpha_tab = reinterpret_cast<float*>(smem + STAGES * kStageBytes + 4 * kStripBytes) + wave * WN;
@@ -1261,10 +1338,10 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
     constexpr int kStages = 3;
     const dim3 grid((unsigned)big_tiles), block(256);
     const bool gates = cs.decay_hi > cs.decay_lo || cs.write_hi > cs.write_lo;
-#define NVFP4_STREAM(BF16, GATES)                                                                    \
-  gemm_stream_kernel<kStages, BF16, GATES><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, \
-                                                                       w_scales, cs, (int)M, (int)N,  \
-                                                                       (int)K, y, ldy)
+#define NVFP4_STREAM(BF16, GATES)                                                                           \
+  gemm_stream_kernel<kStages, BF16, GATES, false><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, \
+                                                                              w_scales, cs, (int)M, (int)N,  \
+                                                                              (int)K, y, ldy, SwigluOut{})
     if (out_bf16) {
       if (gates) NVFP4_STREAM(true, true);
       else NVFP4_STREAM(true, false);
@@ -1286,6 +1363,19 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   }
   return launch_tiles<128, 128, 64, 64>(a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y,
                                         out_bf16, ldy, aligned, stream);
+}
+
+hipError_t launch_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                                       const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
+                                       int64_t M, int64_t F, int64_t K, const SwigluOut& out, hipStream_t stream) {
+  ColScales cs{};
+  cs.gs = w_gs;
+  cs.n = 1;
+  cs.end[0] = (int)(2 * F);
+  const int64_t tiles = ((M + 255) / 256) * ((2 * F + 255) / 256);
+  gemm_stream_kernel<3, false, false, true><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(
+      a_codes, a_scales, a_gs, w_codes, w_scales, cs, (int)M, (int)(2 * F), (int)K, nullptr, 0, out);
+  return hipGetLastError();
 }
 
 bool quantize_gemm_fused_fits(int64_t M, int64_t N, int64_t K, bool in_bf16) {

@@ -31,6 +31,23 @@ struct ColScales {
   const float* dt_bias;
 };
 
+// Output of the SwiGLU + quantize epilogue: h = silu(gate) * up of a GEMM
+// whose weight rows are [gate (F rows); up (F rows)], quantized with the
+// given tensor scale into codes [M x F/2] and scales [M x F/16], and
+// optionally written in fp32 to h [M x ldh].
+struct SwigluOut {
+  const float* gs;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* h;
+  int64_t ldh;
+  int F;
+};
+
+hipError_t launch_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                                       const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
+                                       int64_t M, int64_t F, int64_t K, const SwigluOut& out, hipStream_t stream);
+
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
                        const uint8_t* w_codes, const uint8_t* w_scales, const ColScales& cs,
                        int64_t M, int64_t N, int64_t K, void* y, bool out_bf16, int64_t ldy,

@@ -243,6 +243,24 @@ def sigmoid(z) -> np.ndarray:
     return np.where(z >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
 
 
+def silu(z) -> np.ndarray:
+    """z * sigmoid(z) in fp64."""
+    z = np.asarray(z, dtype=np.float64)
+    return z * sigmoid(z)
+
+
+def gemm_swiglu_ref(a_codes, a_scales, g_a, w_codes, w_scales, g_w):
+    """The MLP gate/up projection followed by SwiGLU, fp64: with W = [gate (F
+    rows); up (F rows)], Y = gemm_ref(A, W) and h = silu(Y_gate) * Y_up.  The
+    activation between the two MLP projections is not on the pages; SwiGLU
+    is the reading adopted for it.  Returns (H, G, U, SG, SU): h, the gate
+    and up outputs, and their error allowances' Sabs from gemm_ref."""
+    y, sabs = gemm_ref(a_codes, a_scales, g_a, w_codes, w_scales, g_w)
+    f = y.shape[1] // 2
+    g, u = y[:, :f], y[:, f:]
+    return silu(g) * u, g, u, sabs[:, :f], sabs[:, f:]
+
+
 def gdn_decay_gate(v, a_log, dt_bias) -> np.ndarray:
     """Log-space decay gate of a GDN head: g = -exp(A_log) * softplus(a + dt_bias)
     ([PX] "Gated DeltaNet Mechanics"); v holds the a-projection outputs

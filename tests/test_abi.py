@@ -229,3 +229,27 @@ def test_gdn_recurrence_rejects_bad_arguments(lib):
     assert gd(lib, T=0, x=None) == OK                        # nothing to do
     assert gd(lib, T=0, cols=(0, 256, -1, 1024, 1028)) == OK  # v = 0 is allowed
     assert lib.nvfp4_last_hip_error() == 0
+
+
+def sq(lib, ptrs=None, M=4, F=64, K=128, hgs=P16, hc=P16, hs=P16, h=None, ldh=0):
+    p = ptrs or [P16] * 6
+    return lib.nvfp4_gemm_swiglu_quantize(*p, M, F, K, hgs, hc, hs, h, ldh, None)
+
+
+def test_gemm_swiglu_quantize_rejects_bad_arguments(lib):
+    assert sq(lib, F=96) == SHAPE            # F % 64
+    assert sq(lib, K=64) == SHAPE            # K % 128
+    assert sq(lib, M=-1) == SHAPE
+    assert sq(lib, h=P16, ldh=63) == SHAPE   # ldh < F
+    assert sq(lib, M=1 << 20, K=1 << 13) == SHAPE   # M K / 2 >= 2^31
+    assert sq(lib, hgs=None) == NULL
+    assert sq(lib, hc=None) == NULL
+    for i in range(6):
+        p = [P16] * 6
+        p[i] = None
+        assert sq(lib, ptrs=p) == NULL
+    assert sq(lib, hc=ctypes.c_void_p(0x10004)) == ALIGN
+    assert sq(lib, h=ctypes.c_void_p(0x10008), ldh=64) == ALIGN
+    assert sq(lib, h=P16, ldh=66) == ALIGN   # ldh % 4
+    assert sq(lib, M=0, ptrs=[None] * 6, hgs=None, hc=None, hs=None) == OK
+    assert lib.nvfp4_last_hip_error() == 0

@@ -519,3 +519,22 @@ def test_segmented_gates_are_the_segmented_gemm_then_the_gate_functions():
     # the decay module may come first and the write module before it
     G3, _, _ = ref.gemm_segmented_gates_ref(*a, wc, wsc, gs, rows, 0, rng.uniform(0, 1, 24), np.zeros(24), 1)
     assert np.all(G3[:, :24] < 0) and np.all((G3[:, 24:40] > 0) & (G3[:, 24:40] < 1))
+
+
+def test_silu_identities_and_swiglu_composition():
+    import math
+    z = np.linspace(-40.0, 40.0, 321)
+    assert ref.silu(0.0) == 0.0
+    assert np.allclose(ref.silu(z) - ref.silu(-z), z, rtol=0, atol=1e-12)       # z (s(z) + s(-z)) = z
+    assert abs(ref.silu(math.log(3.0)) - 0.75 * math.log(3.0)) < 1e-15
+    assert abs(ref.silu(40.0) - 40.0) < 1e-15 and abs(ref.silu(-40.0)) < 1e-15
+    h = 1e-6
+    d = (ref.silu(z + h) - ref.silu(z - h)) / (2 * h)
+    assert np.all(d <= 1.1) and np.all(d >= -0.1)                                  # the slope bound tests use
+    rng = np.random.default_rng(9)
+    a = ref.quantize(rng.standard_normal((3, 64)).astype(np.float32))
+    w = ref.quantize((rng.standard_normal((2 * 32, 64)) * 0.2).astype(np.float32))
+    H, G, U, SG, SU = ref.gemm_swiglu_ref(*a, *w)
+    Y, S = ref.gemm_ref(*a, *w)
+    assert np.array_equal(G, Y[:, :32]) and np.array_equal(U, Y[:, 32:]) and np.array_equal(SU, S[:, 32:])
+    assert np.allclose(H, G / (1 + np.exp(-G)) * U, rtol=1e-13, atol=1e-300)
