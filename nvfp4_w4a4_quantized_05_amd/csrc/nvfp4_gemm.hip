@@ -42,6 +42,11 @@ constexpr int kRowBytes = kBK / 2;    // 64 code bytes per row per step
 constexpr int kLdsRow = kRowBytes + 16;  // padded LDS row stride: conflict-free 16-byte reads
 constexpr int kScaleBytes = kBK / 16;    // 8 scale bytes per row per step
 constexpr size_t kDecodeMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+// Waves per decode workgroup; each takes a contiguous part of K.  Eight
+// (two per SIMD, M <= 16 without spills) measured about 10% slower than four
+// at N = 12288 / 12384, K = 5120: each wave then has 2-3 tiles, so the ring's
+// fill and the wider reduction weigh more.
+constexpr int kDecodeWaves = 4;
 // In-kernel activation quantization of the decode kernel: at most this many
 // rows, and K up to kFusedMaxK.  The kernel handles up to 4 rows; at 3 and 4
 // the quantize ALU work outgrows the time the weight loads leave free, and a
@@ -851,9 +856,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
 //
 // A workgroup owns NB 16-row MFMA blocks of weight rows (the launcher picks
 // NB = 1..4 so that the workgroups fill the 256 CUs with the fewest rounds:
-// N = 12288 gives 256 workgroups of 48 rows) and all M rows of A; its 4
-// waves split K into quarters of nt tiles of 256 values.  Codes go straight into registers, D
-// tiles ahead; only the scale bytes and the final reduction use LDS.
+// N = 12288 gives 256 workgroups of 48 rows) and all M rows of A; its
+// kDecodeWaves (4) waves split K into contiguous parts of nt tiles of 256
+// values.  Codes go straight into registers, D tiles ahead; only the scale
+// bytes and the final reduction use LDS.
 //
 //  * One code load reads 8 rows x 128 contiguous bytes (lane L: row L % 8,
 //    16-byte chunk L / 8), the pattern that reaches full HBM read bandwidth;
@@ -876,7 +882,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
 //    quantize kernel, so the same bytes), and reads its A operand back in
 //    MFMA layout.  That ALU work overlaps the weight loads in flight, which
 //    bound the loop, and saves the separate quantize launch of a decode step.
-//  * The four K-quarter partial sums are added through LDS in a fixed order
+//  * The waves' K-part partial sums are added through LDS in a fixed order
 //    (deterministic), then scaled by RN32(g_a g_w) and stored.
 // MB16 = number of 16-row blocks of A (1, 2 or 4); NB = number of 16-row
 // blocks of W; D = tiles in flight.
@@ -889,7 +895,7 @@ template <int MB16, int NB, int kXIn>
 constexpr int decode_wave_bytes_per_tile() { return decode_scale_rows<MB16, NB>() * 16 + (kXIn ? 16 * MB16 * 128 : 0); }
 
 template <int MB16, int NB, int D, int kXIn>
-__global__ __launch_bounds__(256) void gemm_decode_kernel(
+__global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const ColScales cs,
     int M, int N, int K, void* __restrict__ y, int64_t ldy, bool out_bf16, int nt_max,
@@ -908,7 +914,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
   const int n0 = blockIdx.x * NW;
   const uint32_t row_bytes = (uint32_t)K / 2, srow_bytes = (uint32_t)K / 16;
   const int kt = K / 256;
-  const int t0 = (kt * wave) / 4, nt = (kt * (wave + 1)) / 4 - t0;
+  const int t0 = (kt * wave) / kDecodeWaves, nt = (kt * (wave + 1)) / kDecodeWaves - t0;
   const int run = nt * kTileScales;  // scale bytes per row in this wave's range
   uint8_t* const wsl = dsmem + wave * decode_wave_bytes_per_tile<MB16, NB, kXIn>() * nt_max;  // [NW rows][run]
   uint8_t* const asl = wsl + NW * run;                                                    // [MA rows][run]
@@ -1149,10 +1155,10 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
       }
   }
 
-  // fixed-order sum of the 4 K quarters through LDS (the scale area is free
-  // once every wave has passed the barrier)
+  // fixed-order sum of the waves' K parts through LDS (the scale area is
+  // free once every wave has passed the barrier)
   __syncthreads();
-  float* red = reinterpret_cast<float*>(dsmem);  // [3 waves][NB][MB16][4][64]
+  float* red = reinterpret_cast<float*>(dsmem);  // [kDecodeWaves - 1 waves][NB][MB16][4][64]
   if (wave > 0) {
 #pragma unroll
     for (int j = 0; j < NB; ++j)
@@ -1181,7 +1187,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
         for (int v = 0; v < 4; ++v) {
           float t = acc[j][b][v];
 #pragma unroll
-          for (int w = 0; w < 3; ++w) t += red[((w * NB + j) * MB16 + b) * 256 + v * 64 + lane];
+          for (int w = 0; w < kDecodeWaves - 1; ++w) t += red[((w * NB + j) * MB16 + b) * 256 + v * 64 + lane];
           o[v] = t * (s_first == s_last ? alpha_u : col_alpha(g_a, cs, n + v));
           if (gated) o[v] = col_gate(cs, n + v, o[v]);
         }
@@ -1224,8 +1230,8 @@ bool allow_lds(const void* fn, size_t bytes) {
 // buffer if larger.
 template <int MB16, int NB, int kXIn>
 size_t decode_lds_bytes(int nt_max) {
-  const size_t scales = (size_t)4 * decode_wave_bytes_per_tile<MB16, NB, kXIn>() * nt_max;
-  const size_t red = (size_t)3 * NB * MB16 * 4 * 64 * sizeof(float);
+  const size_t scales = (size_t)kDecodeWaves * decode_wave_bytes_per_tile<MB16, NB, kXIn>() * nt_max;
+  const size_t red = (size_t)(kDecodeWaves - 1) * NB * MB16 * 4 * 64 * sizeof(float);
   return scales > red ? scales : red;
 }
 
@@ -1290,9 +1296,9 @@ template <int kXIn>
 bool launch_decode(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs, const void* x, int64_t ldx,
                    const uint8_t* w_codes, const uint8_t* w_scales, const ColScales& cs, int64_t M, int64_t N,
                    int64_t K, void* y, bool out_bf16, int64_t ldy, hipStream_t stream, hipError_t* err) {
-  const int nt_max = (int)((K / 256 + 3) / 4);
+  const int nt_max = (int)((K / 256 + kDecodeWaves - 1) / kDecodeWaves);
   const int nb = decode_blocks_per_wg(N);
-  const dim3 grid((unsigned)(((N + 15) / 16 + nb - 1) / nb)), block(256);
+  const dim3 grid((unsigned)(((N + 15) / 16 + nb - 1) / nb)), block(64 * kDecodeWaves);
   const int m = (int)M, n = (int)N, k = (int)K;
 #define NVFP4_DECODE_NB(MB, NBB, DD)                                                                              \
   do {                                                                                                             \
@@ -1353,7 +1359,7 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
     return hipGetLastError();
   }
   // decode: buffer offsets of rows up to N + 63 must stay below 2^31, and
-  // the scale runs of the longest K quarter must fit in LDS
+  // the scale runs of the longest K part must fit in LDS
   const bool fits_decode = (N + 64) * (K / 2) < ((int64_t)1 << 31) && M * (K / 2) < ((int64_t)1 << 31);
   if (aligned && fits_decode && M <= 64 && K % 256 == 0) {
     hipError_t err = hipSuccess;
@@ -1382,7 +1388,8 @@ bool quantize_gemm_fused_fits(int64_t M, int64_t N, int64_t K, bool in_bf16) {
   if (!in_bf16 || M < 1 || M > kFusedRows || K % 256 != 0) return false;
   if (K > kFusedMaxK) return false;
   if ((N + 64) * (K / 2) >= ((int64_t)1 << 31)) return false;
-  return decode_lds_for<1, 1>(decode_blocks_per_wg(N), (int)((K / 256 + 3) / 4)) <= kDecodeMaxLds;
+  return decode_lds_for<1, 1>(decode_blocks_per_wg(N), (int)((K / 256 + kDecodeWaves - 1) / kDecodeWaves)) <=
+         kDecodeMaxLds;
 }
 
 hipError_t launch_quantize_gemm_fused(const void* x, bool in_bf16, int64_t ldx, const float* a_gs,
