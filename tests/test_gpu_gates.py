@@ -75,7 +75,7 @@ def _case(M, K, rows, decay, write, seed, rows_sample=None):
                                f"y={yv[:, gate_cols][tuple(bad[0])]!r} G={G[:, gate_cols][tuple(bad[0])]!r}")
 
 
-@pytest.mark.parametrize("M", [1, 7, 40])
+@pytest.mark.parametrize("M", [1, 7, 20, 40])
 @pytest.mark.parametrize("rows", [(120, 48, 48, 40), (256, 128, 48, 48)])
 def test_gates_decode_kernel(M, rows):
     print(f"[gates] decode M={M} rows={rows}", flush=True)

@@ -107,3 +107,37 @@ def test_single_token_and_empty():
     dev = need_gpu()
     nv.gdn_recurrence(torch.zeros((0, LDX), dtype=torch.float32, device=dev), **LAYOUT, n_qk_heads=2, n_v_heads=4)
     torch.cuda.synchronize()
+
+
+def _check_heads(T, n_qk, n_v, seed):
+    """The same checks for another head layout: q | k | v | g | beta packed
+    from column 0, with n_qk q/k heads and n_v value heads."""
+    dev = need_gpu()
+    rng = np.random.default_rng(seed)
+    q_col, k_col, v_col = 0, n_qk * D, 2 * n_qk * D
+    g_col = v_col + n_v * D
+    b_col = g_col + n_v
+    x = np.zeros((T, b_col + n_v), np.float32)
+    x[:, :g_col] = rng.standard_normal((T, g_col))
+    x[:, g_col:b_col] = -np.exp(rng.uniform(0, 2.7, n_v)) * np.log1p(np.exp(rng.standard_normal((T, n_v)) - 4))
+    x[:, b_col:] = 1 / (1 + np.exp(-rng.standard_normal((T, n_v))))
+    so = torch.empty((n_v, D, D), dtype=torch.float32, device=dev)
+    o = torch.empty((T, n_v * D), dtype=torch.float32, device=dev)
+    nv.gdn_recurrence(torch.from_numpy(x).to(dev), q_col=q_col, k_col=k_col, v_col=v_col, g_col=g_col,
+                      beta_col=b_col, n_qk_heads=n_qk, n_v_heads=n_v, state_out=so, o=o)
+    torch.cuda.synchronize()
+    q, k, v, g, beta = G.split_projection_rows(x, q_col, k_col, v_col, g_col, b_col, n_qk, n_v)
+    O, S, _, NR = G.gdn_recurrence_ref(q, k, v, g, beta)
+    M = np.maximum.accumulate(np.sqrt(NR) + beta * np.linalg.norm(v, axis=2), axis=0)
+    e_S = np.arange(1, T + 1)[:, None] * (D + 16) * 2.0 ** -24 * M
+    err = np.linalg.norm((so.cpu().numpy() - S).reshape(n_v, -1), axis=1)
+    assert np.all(err <= e_S[-1]), f"state error {err} > {e_S[-1]}"
+    oe = np.linalg.norm(o.cpu().numpy().reshape(T, n_v, D) - O, axis=2)
+    assert np.all(oe <= (e_S + D * 2.0 ** -24 * np.sqrt(NR)) / np.sqrt(D))
+
+
+@pytest.mark.parametrize("T,n_qk,n_v", [(6, 2, 2), (7, 1, 4), (130, 3, 3), (203, 2, 8)])
+def test_recurrence_head_layouts_and_token_remainders(T, n_qk, n_v):
+    # T % 4 = 2, 3, 2, 3: the loop runs in groups of 4 tokens
+    print(f"[gdn] T={T} n_qk={n_qk} n_v={n_v}", flush=True)
+    _check_heads(T, n_qk, n_v, seed=T)

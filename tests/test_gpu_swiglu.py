@@ -20,7 +20,7 @@ from workloads import activations, normal_weights
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M,F,K,sample", [(300, 192, 256, None), (1000, 512, 1024, None),
+@pytest.mark.parametrize("M,F,K,sample", [(300, 192, 256, None), (257, 64, 128, None), (1000, 512, 1024, None),
                                           (4096, 17408, 5120, (0, 1, 255, 2049, 4095))])
 def test_swiglu_quantize_epilogue(M, F, K, sample):
     dev = need_gpu()
