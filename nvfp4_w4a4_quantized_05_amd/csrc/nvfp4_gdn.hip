@@ -15,15 +15,18 @@
 // in-projection with its gate epilogue writes exactly such rows).  Value
 // head h reads q/k head h * n_qk / n_v.
 //
-// One workgroup of 256 threads per value head, d_k = d_v = 128.  Thread t
-// owns column j = t % 128 of S and rows 64 (t / 128) .. + 63, in registers.
-// Per token:
+// One workgroup of 1024 threads (16 waves, four per SIMD) per value head,
+// d_k = d_v = 128.  Thread t owns column j = t % 128 of S and its rows
+// 16 (t / 128) .. + 15, in registers.  Per token:
 //   * k and q (2 x 128 values) were staged in LDS during the previous token,
-//     one value per thread, with their squared norms reduced per wave;
-//   * u_j: each thread sums its 64 rows, the two halves meet in LDS (barrier);
-//   * the update of the thread's 64 state values, then the partial of o_j;
-//   * the next token's k / q go to the other LDS buffer, and the halves of
+//     one value per thread of waves 0-3, with their squared norms reduced
+//     per wave;
+//   * u_j: each thread sums its 16 rows, the eight parts meet in LDS (barrier);
+//   * the update of the thread's 16 state values, then its part of o_j;
+//   * the next token's k / q go to the other LDS buffer, and the parts of
 //     o_j meet (barrier).
+// (Two parts of 64 rows on 256 threads took 1.75 us per token, four parts
+// 1.39 us, eight 1.32 us.)
 // Loads of the projection rows run 4 tokens ahead in registers (a ring of
 // slots indexed at compile time), so the sequential loop does not wait on
 // memory.
@@ -37,46 +40,63 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kD = 128;       // head dimension (d_k = d_v)
+constexpr int kSplit = 8;     // threads per state column: each holds kD / kSplit rows
+constexpr int kRows = kD / kSplit;
+constexpr int kThreads = kD * kSplit;
 constexpr int kAhead = 4;     // tokens of loads in flight
 constexpr float kNormEps = 1e-6f;
 
+// Sum over the wave's 64 lanes with DPP (no LDS round trips): quad
+// permutes, half-row and row mirrors give every lane its 16-lane row's sum,
+// then row broadcasts 15 and 31 carry rows 0-2 into row 3; lane 63 holds the
+// total, returned to every lane.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_add<0x140, 0xF>(v);  // row_mirror
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-__global__ __launch_bounds__(256) void gdn_recurrence_kernel(
+__global__ __launch_bounds__(kThreads) void gdn_recurrence_kernel(
     const float* __restrict__ x, int64_t ldx, int q_col, int k_col, int v_col, int g_col, int b_col, int T,
     int n_qk, int n_v, const float* __restrict__ s_in, float* __restrict__ s_out, float* __restrict__ o,
     int64_t ldo, float* __restrict__ norms, const int* __restrict__ snap_steps, int n_snaps,
     float* __restrict__ snaps) {
   const int h = blockIdx.x;              // value head
   const int hk = h / (n_v / n_qk);       // its q / k head
-  const int tid = threadIdx.x, j = tid & (kD - 1), hf = tid >> 7;
+  const int tid = threadIdx.x, j = tid & (kD - 1), hf = tid >> 7;  // column, row part
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
   __shared__ __attribute__((aligned(16))) float kq[2][2 * kD];  // [buffer][k 0..127 | q 128..255]
   __shared__ float nrm[2][4];                                   // [buffer][wave]: k (waves 0, 1), q (2, 3)
-  __shared__ float part[2][2][kD];                              // [u | o][half][column]
-  __shared__ float nsum[4];
+  __shared__ float part[2][kSplit][kD];                         // [u | o][row part][column]
+  __shared__ float nsum[kThreads / 64];
 
-  float S[64];
+  float S[kRows];
   {
     const float* si = s_in ? s_in + (int64_t)h * kD * kD : nullptr;
 #pragma unroll
-    for (int r = 0; r < 64; ++r) S[r] = si ? si[(64 * hf + r) * kD + j] : 0.0f;
+    for (int r = 0; r < kRows; ++r) S[r] = si ? si[(kRows * hf + r) * kD + j] : 0.0f;
   }
 
-  // this thread's staged element (k for tid < 128, q for the rest), its
-  // value-column and its head's gate columns
+  // this thread's staged element (k for tid < 128, q for tid < 256; the
+  // other threads stage nothing), its value column and its head's gate
+  // columns
+  const bool stager = tid < 2 * kD;
   const int64_t sc = (tid < kD ? k_col : q_col) + (int64_t)hk * kD + j;
   const int64_t vc = v_col >= 0 ? v_col + (int64_t)h * kD + j : -1;
   float p_s[kAhead], p_v[kAhead], p_g[kAhead], p_b[kAhead];
   auto fetch = [&](int t, float& s, float& v, float& g, float& b) {
     if (t < T) {
       const float* row = x + (int64_t)t * ldx;
-      s = row[sc];
+      s = stager ? row[sc] : 0.0f;
       v = vc >= 0 ? row[vc] : 0.0f;
       g = row[g_col + h];
       b = row[b_col + h];
@@ -88,9 +108,11 @@ __global__ __launch_bounds__(256) void gdn_recurrence_kernel(
   for (int a = 0; a < kAhead; ++a) fetch(a, p_s[a], p_v[a], p_g[a], p_b[a]);
 
   auto stage = [&](float s, int buf) {
-    kq[buf][tid] = s;
-    const float sq = wave_sum(s * s);
-    if (lane == 0) nrm[buf][wave] = sq;
+    if (stager) {  // waves 0-3 (uniform per wave)
+      kq[buf][tid] = s;
+      const float sq = wave_sum(s * s);
+      if (lane == 0) nrm[buf][wave] = sq;
+    }
   };
   stage(p_s[0], 0);
   __syncthreads();
@@ -110,21 +132,24 @@ __global__ __launch_bounds__(256) void gdn_recurrence_kernel(
       const int buf = t & 1;
       const float v_t = p_v[a], g_t = p_g[a], b_t = p_b[a];
 
-      const float* kv = &kq[buf][64 * hf];
-      const float* qv = &kq[buf][kD + 64 * hf];
+      const float* kv = &kq[buf][kRows * hf];
+      const float* qv = &kq[buf][kD + kRows * hf];
       const float rk = 1.0f / fmaxf(sqrtf(nrm[buf][0] + nrm[buf][1]), kNormEps);
       const float rq = rsd / fmaxf(sqrtf(nrm[buf][2] + nrm[buf][3]), kNormEps);
 
       // u_j = S_{t-1}^T k (k not yet normalized: scaled by rk below); eight
-      // independent partial sums, so the sum is not one chain of 64 FMAs
+      // independent partial sums, so the sum is not one long chain of FMAs
       float acc[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 64; ++r) acc[r & 7] = fmaf(S[r], kv[r], acc[r & 7]);
+      for (int r = 0; r < kRows; ++r) acc[r & 7] = fmaf(S[r], kv[r], acc[r & 7]);
       part[0][hf][j] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
       __syncthreads();
-      const float u = (part[0][0][j] + part[0][1][j]) * rk;
+      float usum = 0.0f;
+#pragma unroll
+      for (int p = 0; p < kSplit; ++p) usum += part[0][p][j];
+      const float u = usum * rk;
       const float alpha = expf(g_t);
       const float dk = b_t * (v_t - u) * rk;  // beta (v - u), times 1 / |k| for the raw k below
 
@@ -132,7 +157,7 @@ __global__ __launch_bounds__(256) void gdn_recurrence_kernel(
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 64; ++r) {
+      for (int r = 0; r < kRows; ++r) {
         S[r] = fmaf(kv[r], dk, alpha * S[r]);
         acc[r & 7] = fmaf(S[r], qv[r], acc[r & 7]);
       }
@@ -141,7 +166,7 @@ __global__ __launch_bounds__(256) void gdn_recurrence_kernel(
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 64; ++r) acc[r & 7] = fmaf(S[r], S[r], acc[r & 7]);
+        for (int r = 0; r < kRows; ++r) acc[r & 7] = fmaf(S[r], S[r], acc[r & 7]);
         const float ps = wave_sum(((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7])));
         if (lane == 0) nsum[wave] = ps;
       }
@@ -149,12 +174,22 @@ __global__ __launch_bounds__(256) void gdn_recurrence_kernel(
       fetch(t + kAhead, p_s[a], p_v[a], p_g[a], p_b[a]);
       __syncthreads();
 
-      if (o && hf == 0) o[(int64_t)t * ldo + (int64_t)h * kD + j] = (part[1][0][j] + part[1][1][j]) * rq;
-      if (norms && tid == 0) norms[(int64_t)t * n_v + h] = (nsum[0] + nsum[1]) + (nsum[2] + nsum[3]);
+      if (o && hf == 0) {
+        float osum = 0.0f;
+#pragma unroll
+        for (int p = 0; p < kSplit; ++p) osum += part[1][p][j];
+        o[(int64_t)t * ldo + (int64_t)h * kD + j] = osum * rq;
+      }
+      if (norms && tid == 0) {
+        float ns = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) ns += nsum[w];
+        norms[(int64_t)t * n_v + h] = ns;
+      }
       if (t == next_snap) {
         float* dst = snaps + ((int64_t)snap_i * n_v + h) * kD * kD;
 #pragma unroll
-        for (int r = 0; r < 64; ++r) dst[(64 * hf + r) * kD + j] = S[r];
+        for (int r = 0; r < kRows; ++r) dst[(kRows * hf + r) * kD + j] = S[r];
         ++snap_i;
         next_snap = snap_i < n_snaps ? snap_steps[snap_i] : -1;
       }
@@ -163,7 +198,7 @@ __global__ __launch_bounds__(256) void gdn_recurrence_kernel(
   if (s_out) {
     float* so = s_out + (int64_t)h * kD * kD;
 #pragma unroll
-    for (int r = 0; r < 64; ++r) so[(64 * hf + r) * kD + j] = S[r];
+    for (int r = 0; r < kRows; ++r) so[(kRows * hf + r) * kD + j] = S[r];
   }
 }
 
@@ -173,7 +208,7 @@ hipError_t launch_gdn_recurrence(const float* x, int64_t ldx, int64_t q_col, int
                                  int64_t g_col, int64_t b_col, int64_t T, int n_qk, int n_v, const float* s_in,
                                  float* s_out, float* o, int64_t ldo, float* norms, const int* snap_steps,
                                  int n_snaps, float* snaps, hipStream_t stream) {
-  gdn_recurrence_kernel<<<dim3((unsigned)n_v), dim3(256), 0, stream>>>(
+  gdn_recurrence_kernel<<<dim3((unsigned)n_v), dim3(kThreads), 0, stream>>>(
       x, ldx, (int)q_col, (int)k_col, (int)v_col, (int)g_col, (int)b_col, (int)T, n_qk, n_v, s_in, s_out, o, ldo,
       norms, snap_steps, n_snaps, snaps);
   return hipGetLastError();
