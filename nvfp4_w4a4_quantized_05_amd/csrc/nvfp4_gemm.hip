@@ -1155,68 +1155,76 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
       }
   }
 
-  // fixed-order sum of the waves' K parts through LDS (the scale area is
-  // free once every wave has passed the barrier)
+  // Epilogue, compact on purpose: fully unrolled over every accumulator
+  // block it was over 60 KB of straight-line code at MB16 = NB = 4, and
+  // fetching it took longer than the main loop.  Every wave writes its K
+  // part's sums to LDS (the scale area is free once all waves have passed
+  // the barrier): part[w][m][c], m < MA rows of A, c < NW weight rows, the
+  // 16-byte column quads of row m XOR-swizzled by m so that the 16 lanes of
+  // one write or read phase hit distinct banks.  Then the 256 threads add
+  // the four parts in a fixed order (deterministic), scale by RN32(g_a g_w)
+  // and store 4 consecutive columns each, rows of NW columns contiguous.
+  // The swizzle stays inside aligned groups of kSwz quads, kSwz the largest
+  // power of two dividing the quads per row.
+  constexpr int kQuads = NW / 4;                            // column quads per row
+  constexpr int kSwz = kQuads & -kQuads;
+  constexpr int kRowsPerPass = 64 * kDecodeWaves / kQuads;  // rows per pass of the 256 threads
+  auto part_at = [&](int w, int m, int quad) -> floatx4_t* {
+    return reinterpret_cast<floatx4_t*>(dsmem) + ((w * MA + m) * kQuads + (quad ^ (m & (kSwz - 1))));
+  };
   __syncthreads();
-  float* red = reinterpret_cast<float*>(dsmem);  // [kDecodeWaves - 1 waves][NB][MB16][4][64]
-  if (wave > 0) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int b = 0; b < MB16; ++b)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) red[(((wave - 1) * NB + j) * MB16 + b) * 256 + v * 64 + lane] = acc[j][b][v];
-  }
+    for (int b = 0; b < MB16; ++b) *part_at(wave, 16 * b + q, 4 * j + g) = acc[j][b];
   __syncthreads();
-  if (wave == 0) {
-    // one tensor scale for the workgroup's columns unless a column range
-    // ends inside them
-    const float g_a = *a_gs;
-    const int s_first = col_range(cs, n0), s_last = col_range(cs, min(n0 + NW, N) - 1);
-    const float alpha_u = g_a * cs.gs[s_first];
-    const bool gated = cols_gated(cs, n0, n0 + NW - 1);
-    const bool vec_ok = (ldy % 4 == 0) && ((uintptr_t)y % 16 == 0);
+
+  const int cq = tid % kQuads;
+  const int n = n0 + 4 * cq;
+  const float g_a = *a_gs;
+  // one tensor scale for the workgroup's columns unless a column range ends
+  // inside them
+  const int s_first = col_range(cs, n0), s_last = col_range(cs, min(n0 + NW, N) - 1);
+  float alpha[4];
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+  for (int v = 0; v < 4; ++v) alpha[v] = s_first == s_last ? g_a * cs.gs[s_first] : col_alpha(g_a, cs, n + v);
+  const bool gated = cols_gated(cs, n0, n0 + NW - 1);
+  const bool vec_ok = (ldy % 4 == 0) && ((uintptr_t)y % 16 == 0) && n + 3 < N;
+  const int m_end = min(MA, M);
+#pragma unroll 1
+  for (int m = tid < kRowsPerPass * kQuads ? tid / kQuads : m_end; m < m_end; m += kRowsPerPass) {
+    floatx4_t t = *part_at(0, m, cq);
 #pragma unroll
-      for (int b = 0; b < MB16; ++b) {
-        const int m = 16 * b + q;
-        const int n = n0 + 16 * j + 4 * g;
-        floatx4_t o;
+    for (int w = 1; w < kDecodeWaves; ++w) t += *part_at(w, m, cq);
+    floatx4_t o;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float t = acc[j][b][v];
+    for (int v = 0; v < 4; ++v) {
+      o[v] = t[v] * alpha[v];
+      if (gated) o[v] = col_gate(cs, n + v, o[v]);
+    }
+    if (out_bf16) {
+      __bf16* dst = reinterpret_cast<__bf16*>(y) + (int64_t)m * ldy + n;
+      if (vec_ok) {
+        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+        bf16x4_t h;
 #pragma unroll
-          for (int w = 0; w < kDecodeWaves - 1; ++w) t += red[((w * NB + j) * MB16 + b) * 256 + v * 64 + lane];
-          o[v] = t * (s_first == s_last ? alpha_u : col_alpha(g_a, cs, n + v));
-          if (gated) o[v] = col_gate(cs, n + v, o[v]);
-        }
-        if (m < M) {
-          if (out_bf16) {
-            __bf16* dst = reinterpret_cast<__bf16*>(y) + (int64_t)m * ldy + n;
-            if (vec_ok && n + 3 < N) {
-              typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-              bf16x4_t h;
+        for (int v = 0; v < 4; ++v) h[v] = (__bf16)o[v];
+        *reinterpret_cast<bf16x4_t*>(dst) = h;
+      } else {
 #pragma unroll
-              for (int v = 0; v < 4; ++v) h[v] = (__bf16)o[v];
-              *reinterpret_cast<bf16x4_t*>(dst) = h;
-            } else {
-#pragma unroll
-              for (int v = 0; v < 4; ++v)
-                if (n + v < N) dst[v] = (__bf16)o[v];
-            }
-          } else {
-            float* dst = reinterpret_cast<float*>(y) + (int64_t)m * ldy + n;
-            if (vec_ok && n + 3 < N) {
-              *reinterpret_cast<floatx4_t*>(dst) = o;
-            } else {
-#pragma unroll
-              for (int v = 0; v < 4; ++v)
-                if (n + v < N) dst[v] = o[v];
-            }
-          }
-        }
+        for (int v = 0; v < 4; ++v)
+          if (n + v < N) dst[v] = (__bf16)o[v];
       }
+    } else {
+      float* dst = reinterpret_cast<float*>(y) + (int64_t)m * ldy + n;
+      if (vec_ok) {
+        *reinterpret_cast<floatx4_t*>(dst) = o;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (n + v < N) dst[v] = o[v];
+      }
+    }
   }
 }
 
@@ -1226,12 +1234,12 @@ bool allow_lds(const void* fn, size_t bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess;
 }
 
-// LDS bytes of a decode launch: the per-wave scale runs, or the reduction
-// buffer if larger.
+// LDS bytes of a decode launch: the per-wave scale runs, or the waves'
+// partial sums if larger.
 template <int MB16, int NB, int kXIn>
 size_t decode_lds_bytes(int nt_max) {
   const size_t scales = (size_t)kDecodeWaves * decode_wave_bytes_per_tile<MB16, NB, kXIn>() * nt_max;
-  const size_t red = (size_t)(kDecodeWaves - 1) * NB * MB16 * 4 * 64 * sizeof(float);
+  const size_t red = (size_t)kDecodeWaves * (16 * NB) * (16 * MB16) * sizeof(float);
   return scales > red ? scales : red;
 }
 
