@@ -49,7 +49,89 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=6144, help="token rows in the CPU oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration) and exit")
+    ap.add_argument("--no-clocks", action="store_true", help="do not sample clocks and power with amd-smi")
+    ap.add_argument("--clock-sampler", metavar="FILE", help=argparse.SUPPRESS)
     return ap.parse_args()
+
+
+def clock_sampler(path):
+    """Child process: append one line "t_mid gfx_mhz mem_mhz socket_w" per
+    `amd-smi metric -p -c` reading of GPU 0 to `path` until `path`.stop exists
+    or the parent is gone (at most 30 minutes).  gfx_mhz is the mean over the
+    XCDs' gfx clocks.  Started before the parent touches the GPU."""
+    import subprocess
+    parent = os.getppid()
+    t_end = time.time() + 1800
+    with open(path, "a") as f:
+        while time.time() < t_end and not os.path.exists(path + ".stop") and os.getppid() == parent:
+            t0 = time.time()
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"], capture_output=True,
+                                   text=True, timeout=10)
+                d = json.loads(r.stdout)
+                g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+                clk = g["clock"]
+                gfx = [v["clk"]["value"] for k, v in clk.items()
+                       if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+                mem = clk.get("mem_0", {}).get("clk", {})
+                pw = g.get("power", {}).get("socket_power", {})
+                f.write(f"{(t0 + time.time()) / 2:.3f} {sum(gfx) / len(gfx):.1f} "
+                        f"{mem.get('value', 'nan') if isinstance(mem, dict) else 'nan'} "
+                        f"{pw.get('value', 'nan') if isinstance(pw, dict) else 'nan'}\n")
+                f.flush()
+            except Exception:  # noqa: BLE001  (no amd-smi, or another format: no samples)
+                time.sleep(1.0)
+            time.sleep(0.05)
+
+
+class Clocks:
+    """amd-smi clock and power samples taken by a child process, read per
+    time window afterwards."""
+
+    def __init__(self, enabled):
+        import subprocess
+        import tempfile
+        self.path = None
+        self.proc = None
+        if not enabled:
+            return
+        fd, self.path = tempfile.mkstemp(prefix="nvfp4_clocks_", suffix=".txt")
+        os.close(fd)
+        try:
+            self.proc = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--clock-sampler", self.path],
+                                         stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+        except Exception:  # noqa: BLE001
+            self.proc = None
+
+    def stop(self):
+        if self.proc is None:
+            return []
+        open(self.path + ".stop", "w").close()
+        try:
+            self.proc.wait(timeout=15)
+        except Exception:  # noqa: BLE001
+            self.proc.kill()
+        rows = []
+        for line in open(self.path):
+            try:
+                rows.append(tuple(float(v) for v in line.split()))
+            except ValueError:
+                pass
+        for f in (self.path, self.path + ".stop"):
+            try:
+                os.remove(f)
+            except OSError:
+                pass
+        return rows
+
+    @staticmethod
+    def window(rows, t0, t1):
+        sel = [r for r in rows if t0 <= r[0] <= t1]
+        if not sel:
+            return None
+        med = lambda i: float(sorted(r[i] for r in sel)[len(sel) // 2])  # noqa: E731
+        return {"samples": len(sel), "gfx_mhz_median": med(1), "gfx_mhz_min": min(r[1] for r in sel),
+                "gfx_mhz_max": max(r[1] for r in sel), "mem_mhz": med(2), "socket_power_w_median": med(3)}
 
 
 def calibrate_copy():
@@ -84,6 +166,9 @@ def measured_traffic(per_launch_bytes_alg):
 
 def main():
     args = parse()
+    if args.clock_sampler:
+        clock_sampler(args.clock_sampler)
+        return
     if args.calibrate_copy:
         calibrate_copy()
         return
@@ -92,6 +177,11 @@ def main():
               "(the NVFP4 projections shard over tokens or output columns without exchange; "
               "see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    # a child process, started before this one touches the GPU; not under
+    # rocprofv3, whose tool library would start with it
+    profiled = any(k.startswith("ROCPROF") for k in os.environ)
+    clocks = Clocks(not (args.no_clocks or profiled))
 
     import numpy as np
     import torch
@@ -176,6 +266,8 @@ def main():
             e = evs[s][gi]
             q_ms[g[0]].append(e[0].elapsed_time(e[1]))
             g_ms[g[0]].append(e[1].elapsed_time(e[2]))
+    pct = lambda v: [round(float(np.percentile(v, q)), 4) for q in (10, 50, 90)]  # noqa: E731
+    step_ms = [evs[s][0][0].elapsed_time(evs[s][-1][2]) for s in range(args.steps)]
     flops = {g[0]: 2.0 * T * g[5] * g[6] for g in gemms}
     total_flops = sum(flops.values())
     qbytes = {g[0]: T * g[6] * QUANT_BYTES_PER_ELEM_BF16 for g in gemms}
@@ -187,6 +279,7 @@ def main():
         per[name] = {"M": T, "N": g[5], "K": g[6], "gemm_ms": round(gm, 4),
                      "gemm_tflops": round(flops[name] / gm / 1e9, 1),
                      "gemm_frac_of_peak": round(flops[name] / gm / 1e9 / PEAK_FP16_MFMA_TFLOPS, 4),
+                     "gemm_ms_p10_p50_p90": pct(g_ms[name]),
                      "quantize_ms": round(qm, 4),
                      "quantize_gbps": round(qbytes[name] / qm / 1e6, 1)}
     gemm_ms_total = sum(float(np.mean(g_ms[n])) for n in g_ms)
@@ -207,6 +300,39 @@ def main():
     roofline_q = {"bound": "hbm", "achieved": round(q_ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                   "frac": round(q_ach / PEAK_HBM_GBPS, 4),
                   "kernel": "quantize X_d 32768x17408 bf16 (2.5625 B/value)"}
+
+    # clocks: the timed steps last well under a second, shorter than one
+    # amd-smi reading, so the gate/up GEMM also runs alone for 3 s while the
+    # sampler reads the gfx clock and the socket power
+    t_sus = None
+    if clocks.proc is not None:
+        t_sus0 = time.time()
+        gu = gemms[2]
+        while time.time() - t_sus0 < 3.0:
+            for _ in range(10):
+                nv.gemm(qbuf[2][0], qbuf[2][1], calib[2], gu[2], gu[3], gu[4], out_dtype=torch.bfloat16, out=ys[2])
+            torch.cuda.synchronize()
+        t_sus = (t_sus0, time.time())
+
+    # practical HBM ceiling next to the spec figure: a plain 1 GiB device copy
+    copy_gbps = None
+    try:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 2.0 * (1 << 30) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
+    except Exception:  # noqa: BLE001  (report, never fail the bench on this extra)
+        copy_gbps = None
+    if copy_gbps:
+        roofline_q["practical_peak_copy_gbps"] = round(copy_gbps, 1)
+        roofline_q["frac_of_practical_peak"] = round(q_ach / copy_gbps, 4)
 
     # amax mode (dynamic activation scale) costs one more read of X
     amax_ms = None
@@ -259,6 +385,20 @@ def main():
         "roofline_quantize": roofline_q,
         **extra,
     }
+    samples = clocks.stop()
+    if clocks.proc is not None:
+        # the first half second is left out: the clock is still ramping up
+        during = Clocks.window(samples, t_sus[0] + 0.5, t_sus[1]) if t_sus else None
+        out["clocks"] = {"source": "amd-smi metric -p -c (gfx clock: mean over the XCDs)",
+                         "gate_up_sustained": during,
+                         "note": "read while the gate/up GEMM ran alone for 3 s after the timed steps "
+                                 "(their 0.3 s are too short for the sampler)"}
+        if during:
+            # dense fp16 MFMA: 256 CUs x 4096 flop per clock
+            peak_clk = 256 * 4096 * during["gfx_mhz_median"] * 1e6 / 1e12
+            roofline["peak_at_measured_clock"] = round(peak_clk, 1)
+            roofline["frac_at_measured_clock"] = round(achieved / peak_clk, 4)
+    out["step_ms_p10_p50_p90"] = pct(step_ms)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows, xs, gemms, wq, fused, P, seed)
     print(json.dumps(out), flush=True)
