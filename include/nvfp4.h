@@ -256,11 +256,15 @@ NVFP4_API nvfp4_status_t nvfp4_gemm_swiglu_quantize(const uint8_t* a_codes, cons
  *   state_norms device [T x n_v_heads] fp32 or NULL: |S_t|_F^2 per head
  *   snap_steps, n_snaps, snaps   device: n_snaps strictly increasing token
  *               indices in [0, T) (int32) and [n_snaps x n_v_heads x 128 x
- *               128] fp32 out: S_t after those tokens (steps out of order
- *               are skipped)
+ *               128] fp32 out: S_t after those tokens (a step not above the
+ *               previous one, or not below T, is skipped: its slot is not
+ *               written)
  * Column ranges must lie within ldx (NVFP4_ERR_SHAPE); pointers 4-byte
- * aligned (NVFP4_ERR_ALIGN).  One workgroup per value head runs the tokens
- * in order.  Accuracy: the update operator has norm <= 1, so rounding errors
+ * aligned (NVFP4_ERR_ALIGN).  The columns of each state are independent and
+ * are split over workgroups (8 per value head; one per head when
+ * state_norms is asked for), each running the tokens in order; the per-token
+ * sums are fixed-order, so results are reproducible.  Accuracy: the update
+ * operator has norm <= 1, so rounding errors
  * add without growing: |S_t - S_t(exact)|_F <= t (128 + 16) 2^-24 max_s<=t
  * (|S_s|_F + beta_s |v_s|).
  */

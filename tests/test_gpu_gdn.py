@@ -141,3 +141,40 @@ def test_recurrence_head_layouts_and_token_remainders(T, n_qk, n_v):
     # T % 4 = 2, 3, 2, 3: the loop runs in groups of 4 tokens
     print(f"[gdn] T={T} n_qk={n_qk} n_v={n_v}", flush=True)
     _check_heads(T, n_qk, n_v, seed=T)
+
+
+@pytest.mark.parametrize("want_o,want_norms", [(False, False), (False, True), (True, False), (True, True)])
+def test_recurrence_output_combinations(want_o, want_norms):
+    # each combination of outputs runs its own kernel variant (q is not read
+    # without o; the norms take a whole head per workgroup)
+    print(f"[gdn] T=301 o={want_o} norms={want_norms}", flush=True)
+    dev = need_gpu()
+    x = _rows(301, 11)
+    rng = np.random.default_rng(12)
+    s0 = rng.standard_normal((4, D, D)) * 0.05
+    so = torch.empty((4, D, D), dtype=torch.float32, device=dev)
+    o = torch.empty((301, 4 * D), dtype=torch.float32, device=dev) if want_o else None
+    nr = torch.empty((301, 4), dtype=torch.float32, device=dev) if want_norms else None
+    steps = (0, 63, 64, 200)
+    st = torch.tensor(steps, dtype=torch.int32, device=dev)
+    sn = torch.empty((len(steps), 4, D, D), dtype=torch.float32, device=dev)
+    nv.gdn_recurrence(torch.from_numpy(x).to(dev), **LAYOUT, n_qk_heads=2, n_v_heads=4,
+                      state_in=torch.from_numpy(s0.astype(np.float32)).to(dev), state_out=so, o=o,
+                      state_norms=nr, snap_steps=st, snaps=sn)
+    torch.cuda.synchronize()
+    q, k, v, g, beta = G.split_projection_rows(x, **LAYOUT, n_qk=2, n_v=4)
+    O, S, SN, NR = G.gdn_recurrence_ref(q, k, v, g, beta, s0=s0, snap_steps=steps)
+    norm_S = np.sqrt(NR)
+    M = np.maximum.accumulate(norm_S + beta * np.linalg.norm(v, axis=2), axis=0)
+    M = np.maximum(M, np.linalg.norm(s0.reshape(4, -1), axis=1)[None, :])
+    e_S = np.arange(1, 302)[:, None] * (D + 16) * 2.0 ** -24 * M
+    err = np.linalg.norm((so.cpu().numpy() - S).reshape(4, -1), axis=1)
+    assert np.all(err <= e_S[-1]), f"state error {err} > {e_S[-1]}"
+    for i, s in enumerate(steps):
+        se = np.linalg.norm((sn[i].cpu().numpy() - SN[i]).reshape(4, -1), axis=1)
+        assert np.all(se <= e_S[s]), f"snapshot {s}: {se} > {e_S[s]}"
+    if want_o:
+        oe = np.linalg.norm(o.cpu().numpy().reshape(301, 4, D) - O, axis=2)
+        assert np.all(oe <= (e_S + D * 2.0 ** -24 * norm_S) / np.sqrt(D))
+    if want_norms:
+        assert np.all(np.abs(np.sqrt(nr.cpu().numpy()) - norm_S) <= e_S + 1e-30)
