@@ -428,7 +428,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   constexpr int kLoadsPerStage = 12;                  // vector-memory instructions per wave per stage
   using out_t = typename std::conditional<kOutBf16, __bf16, float>::type;
   constexpr int kEsz = sizeof(out_t);
-  constexpr int kStripRows = 16;                      // output rows staged per pass
+  // output rows staged per pass: a whole 32-row block for bf16 output (every
+  // lane then writes in every pass), 16 for fp32 (LDS room)
+  constexpr int kStripRows = kOutBf16 ? 32 : 16;
   constexpr int kStripRow = WN * kEsz + 16;           // staged row bytes (+16 against bank conflicts)
   constexpr int kStripBytes = kStripRows * kStripRow;
   static_assert(STAGES >= 3, "ring depth");
@@ -789,33 +791,39 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     uint8_t* strip = smem + STAGES * kStageBytes + wave * kStripBytes;
     constexpr int kChunksPerRow = WN * kEsz / 16;
     constexpr int kChunkElems = 16 / kEsz;
+    constexpr int kSubs = 32 / kStripRows;  // passes per 32-row block
+    // the lane's 64 column scales (4 per group of 4 columns), read once
+    floatx4_t al[FN][4];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) al[j][g] = *reinterpret_cast<const floatx4_t*>(alpha_tab + j * 32 + g * 8 + half * 4);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {      // rows r32 in [16 sub, 16 sub + 16)
-        if ((r32 >> 4) == sub) {
-          uint8_t* rowp = strip + (r32 & 15) * kStripRow;
+      for (int sub = 0; sub < kSubs; ++sub) {  // rows r32 in [kStripRows sub, kStripRows (sub + 1))
+        if (kSubs == 1 || (r32 >> 4) == sub) {
+          uint8_t* rowp = strip + (r32 % kStripRows) * kStripRow;
 #pragma unroll
           for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               const int col = j * 32 + g * 8 + half * 4;
-              const floatx4_t al = *reinterpret_cast<const floatx4_t*>(alpha_tab + col);
               if constexpr (kOutBf16) {
                 typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
                 bf4_t o;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) o[t] = (__bf16)(acc[j][i][4 * g + t] * al[t]);
+                for (int t = 0; t < 4; ++t) o[t] = (__bf16)(acc[j][i][4 * g + t] * al[j][g][t]);
                 *reinterpret_cast<bf4_t*>(rowp + col * kEsz) = o;
               } else {
                 floatx4_t o;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) o[t] = acc[j][i][4 * g + t] * al[t];
+                for (int t = 0; t < 4; ++t) o[t] = acc[j][i][4 * g + t] * al[j][g][t];
                 *reinterpret_cast<floatx4_t*>(rowp + col * kEsz) = o;
               }
             }
         }
-        const int grow0 = m0 + wave_m * WM + i * 32 + sub * 16;
+        const int grow0 = m0 + wave_m * WM + i * 32 + sub * kStripRows;
         const int gcol0 = n0 + wave_n * WN;
         constexpr int kQ = kStripRows * kChunksPerRow / 64;
         u32x4_t d[kQ];
