@@ -670,11 +670,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   // Epilogue.  Lane (r32, half) of block (j, i) holds, for output row
   // m = m0 + 128 wave_m + 32 i + r32, the columns n0 + 128 wave_n + 32 j +
   // 8 (v / 4) + 4 half + (v % 4), v = 0..15: four consecutive columns per
-  // group of 4 accumulators.  Rows go through LDS in strips of 16.
-  // RN32(g_a g_w) of the wave's 128 columns goes to a small LDS table; each
-  // group of 4 columns reads its 4 values from there.  When one column range
-  // covers all 128 columns (every plain GEMM, and most tiles of a segmented
-  // one) the table holds one value, found with one lookup.
+  // group of 4 accumulators.  Rows go through LDS in strips of 32 (bf16
+  // output) or 16 (fp32).  RN32(g_a g_w) of the wave's 128 columns goes to a
+  // small LDS table, from which each lane reads the scales of its 64
+  // columns once.  When one column range covers all 128 columns (every plain
+  // GEMM, and most tiles of a segmented one) the table is filled with one
+  // value, found with one lookup.
   const float g_a = *a_gs;
   if constexpr (kSwiglu) {
     // h = silu(g) u of the wave's 64 output columns c_out .. + 63 (v = acc
