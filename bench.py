@@ -788,8 +788,14 @@ def cpu_baseline(rows, xs, gemms, wq, fused, P, seed):
         ref.gemm_ref(*a, wc, ws, wg)
         flops += 2.0 * x.shape[0] * wc.shape[0] * x.shape[1]
     dt = time.perf_counter() - t0
+    full_flops = sum(2.0 * TOKENS * n * k for (_name, _xi, *_rest, n, k) in gemms)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "host_cpus": os.cpu_count(), "kind": "oracle",
+            "host_cpus": os.cpu_count(), "affinity_cpus": affinity, "kind": "oracle",
+            "extrapolated_full_step_s": round(full_flops / (flops / dt), 1),
             "sample": f"first {rows} of {TOKENS} tokens of each input and 1/{frac} of each projection's "
                       f"output features: {flops / 1e9:.1f} GFLOP + {sum(s[0].size for s in samples) / 1e6:.1f}M "
                       f"values quantized in {dt:.1f} s (fp64 numpy oracle, quantize + GEMM + |a*w| sums)"}
