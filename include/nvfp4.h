@@ -240,7 +240,7 @@ NVFP4_API nvfp4_status_t nvfp4_gemm_swiglu_quantize(const uint8_t* a_codes, cons
  * in-projection writes (nvfp4_gemm_segmented_gates, fp32 output).
  *
  *   x           device, [T x ldx] fp32, one row per token (read);
- *               0 < ldx <= 2^23 (NVFP4_ERR_SHAPE otherwise)
+ *               0 < ldx < 2^23 (NVFP4_ERR_SHAPE otherwise)
  *   q_col, k_col   first column of q / k: n_qk_heads heads of 128 values
  *   v_col       first column of v: n_v_heads heads of 128; -1 reads v as 0
  *               (the recurrence then carries a state perturbation alone)

@@ -155,8 +155,8 @@ nvfp4_status_t nvfp4_gdn_recurrence(const float* x, int64_t ldx, int64_t q_col, 
                                     float* snaps, void* stream) {
   try {
     constexpr int64_t kD = 128;
-    // rows of up to 2^23 values: 64 rows of the chunk loads fit one 32-bit buffer range
-    if (T < 0 || T > INT_MAX || ldx <= 0 || ldx > ((int64_t)1 << 23)) return NVFP4_ERR_SHAPE;
+    // rows of fewer than 2^23 values: 64 rows of the chunk loads stay below 2^31 bytes
+    if (T < 0 || T > INT_MAX || ldx <= 0 || ldx >= ((int64_t)1 << 23)) return NVFP4_ERR_SHAPE;
     if (n_qk_heads < 1 || n_v_heads < 1 || n_v_heads > 65535 || n_v_heads % n_qk_heads != 0) return NVFP4_ERR_SHAPE;
     if (q_col < 0 || q_col + n_qk_heads * kD > ldx || k_col < 0 || k_col + n_qk_heads * kD > ldx)
       return NVFP4_ERR_SHAPE;

@@ -222,7 +222,7 @@ def test_gdn_recurrence_rejects_bad_arguments(lib):
     assert gd(lib, cols=(0, 256, -2, 1024, 1028)) == SHAPE
     assert gd(lib, o=P16, ldo=511) == SHAPE                  # ldo < 4 * 128
     assert gd(lib, n_snaps=-1) == SHAPE
-    assert gd(lib, ldx=(1 << 23) + 1) == SHAPE               # rows longer than 2^23 values
+    assert gd(lib, ldx=1 << 23) == SHAPE                     # rows of 2^23 values or more
     assert gd(lib, x=None) == NULL
     assert gd(lib, n_snaps=2, steps=None, snaps=P16) == NULL
     assert gd(lib, x=ctypes.c_void_p(0x10002)) == ALIGN
