@@ -893,7 +893,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
 //    bound the loop, and saves the separate quantize launch of a decode step.
 //  * The waves' K-part partial sums are added through LDS in a fixed order
 //    (deterministic), then scaled by RN32(g_a g_w) and stored.
-// MB16 = number of 16-row blocks of A (1, 2 or 4); NB = number of 16-row
+// MB16 = number of 16-row blocks of A (1 to 4); NB = number of 16-row
 // blocks of W; D = tiles in flight.
 template <int MB16, int NB>
 constexpr int decode_scale_rows() { return 16 * NB + 16 * MB16; }
@@ -1165,7 +1165,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   }
 
   // Epilogue, compact on purpose: fully unrolled over every accumulator
-  // block it was over 60 KB of straight-line code at MB16 = NB = 4, and
+  // block it was about 80 KB of straight-line code at MB16 = NB = 4, and
   // fetching it took longer than the main loop.  Every wave writes its K
   // part's sums to LDS (the scale area is free once all waves have passed
   // the barrier): part[w][m][c], m < MA rows of A, c < NW weight rows, the
@@ -1343,6 +1343,7 @@ bool launch_decode(const uint8_t* a_codes, const uint8_t* a_scales, const float*
   } else {
     if (M <= 16) NVFP4_DECODE(1, 2);
     else if (M <= 32) NVFP4_DECODE(2, 2);
+    else if (M <= 48) NVFP4_DECODE(3, 2);  // rows past M still cost their dequantization
     else NVFP4_DECODE(4, 2);
   }
 #undef NVFP4_DECODE

@@ -99,7 +99,8 @@ def test_large_tile_kernel_with_ragged_edges(shape):
 
 
 @pytest.mark.parametrize("shape", [(64, 100, 17408), (3, 49, 17408), (20, 96, 768), (33, 48, 2560),
-                                   (16, 12288, 4096), (8, 5120, 1024), (2, 12384, 512), (40, 12400, 256)])
+                                   (16, 12288, 4096), (8, 5120, 1024), (2, 12384, 512), (40, 12400, 256),
+                                   (48, 1000, 1280), (49, 640, 512)])
 def test_decode_kernel_k_splits(shape):
     """M <= 64 with K % 256 == 0 takes the decode kernel: K quarters of 0..17
     tiles, full and partial refill rounds, scale runs above 64 KiB of LDS, and
