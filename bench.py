@@ -173,9 +173,9 @@ def main():
         calibrate_copy()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the NVFP4 projections shard over tokens or output columns without exchange; "
-              "see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(the NVFP4 projections would shard over tokens or output columns without exchange). "
+              "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     # a child process, started before this one touches the GPU; not under
