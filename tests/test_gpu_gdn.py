@@ -178,3 +178,26 @@ def test_recurrence_output_combinations(want_o, want_norms):
         assert np.all(oe <= (e_S + D * 2.0 ** -24 * norm_S) / np.sqrt(D))
     if want_norms:
         assert np.all(np.abs(np.sqrt(nr.cpu().numpy()) - norm_S) <= e_S + 1e-30)
+
+
+def test_snapshot_steps_out_of_order_or_past_the_end_are_skipped():
+    # slot i holds S after step i; a step not above the previous one, or not
+    # below T, leaves its slot unwritten
+    print("[gdn] T=40 snapshot steps (5, 3, 10, 10, 39, 40)", flush=True)
+    dev = need_gpu()
+    x = _rows(40, 21)
+    steps = (5, 3, 10, 10, 39, 40)
+    st = torch.tensor(steps, dtype=torch.int32, device=dev)
+    sn = torch.full((len(steps), 4, D, D), np.nan, dtype=torch.float32, device=dev)
+    nv.gdn_recurrence(torch.from_numpy(x).to(dev), **LAYOUT, n_qk_heads=2, n_v_heads=4, snap_steps=st, snaps=sn)
+    torch.cuda.synchronize()
+    q, k, v, g, beta = G.split_projection_rows(x, **LAYOUT, n_qk=2, n_v=4)
+    _, _, SN, NR = G.gdn_recurrence_ref(q, k, v, g, beta, snap_steps=(5, 10, 39))
+    M = np.maximum.accumulate(np.sqrt(NR) + beta * np.linalg.norm(v, axis=2), axis=0)
+    e_S = np.arange(1, 41)[:, None] * (D + 16) * 2.0 ** -24 * M
+    got = sn.cpu().numpy()
+    for slot, ref_i, t in ((0, 0, 5), (2, 1, 10), (4, 2, 39)):
+        err = np.linalg.norm((got[slot] - SN[ref_i]).reshape(4, -1), axis=1)
+        assert np.all(err <= e_S[t]), f"slot {slot} (token {t}): {err} > {e_S[t]}"
+    for slot in (1, 3, 5):
+        assert np.all(np.isnan(got[slot])), f"slot {slot} was written"
