@@ -679,34 +679,33 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   const float g_a = *a_gs;
   if constexpr (kSwiglu) {
     // h = silu(g) u of the wave's 64 output columns c_out .. + 63 (v = acc
-    // RN32(g_a g_w) for both), staged in fp32 in the wave's strip buffer, 16
-    // rows at a time: 16 x 64 values, i.e. 64 blocks of 16, one per lane.
-    // Each lane then quantizes its block with the quantize kernel's
-    // arithmetic and stores 8 code bytes and 1 scale byte (and, if asked,
-    // the 16 fp32 values).
-    static_assert(kStripBytes >= 16 * 64 * 4, "fp32 strip of 16 x 64");
+    // RN32(g_a g_w) for both), staged in fp32 in the wave's strip buffer, 32
+    // rows at a time: 32 x 64 values, i.e. 128 blocks of 16, two per lane.
+    // Each lane then quantizes its blocks with the quantize kernel's
+    // arithmetic and stores 8 code bytes and 1 scale byte per block (and, if
+    // asked, the 16 fp32 values).
+    static_assert(kStripBytes >= 32 * 64 * 4, "fp32 strip of 32 x 64");
     const float alpha = g_a * cs.gs[0];
     const int c_out = n0 / 2 + 64 * wave_n;
     float* fs = reinterpret_cast<float*>(smem + STAGES * kStageBytes + wave * kStripBytes);
     const float hg = *sw.gs, r6 = __builtin_amdgcn_rcpf(6.0f * hg);
-    const int qr = lane >> 2, qb = lane & 3;  // the lane's block: strip row, 16-column block
+    const int qr = lane >> 2, qb = lane & 3;  // the lane's blocks: rows qr and 16 + qr, 16-column block qb
     if (c_out < sw.F) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
+        // the 32 rows of block i, every lane writing its values
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float gv = acc[2 * jj][i][v] * alpha, uv = acc[2 * jj + 1][i][v] * alpha;
+            fs[r32 * 64 + 32 * jj + (v >> 2) * 8 + half * 4 + (v & 3)] = silu_fast(gv) * uv;
+          }
+        __asm__ volatile("" ::: "memory");  // other lanes' values are read below
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-          if ((r32 >> 4) == sub) {
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-              for (int v = 0; v < 16; ++v) {
-                const float gv = acc[2 * jj][i][v] * alpha, uv = acc[2 * jj + 1][i][v] * alpha;
-                fs[(r32 & 15) * 64 + 32 * jj + (v >> 2) * 8 + half * 4 + (v & 3)] = silu_fast(gv) * uv;
-              }
-          }
-          __asm__ volatile("" ::: "memory");  // other lanes' values are read below
           const int row = m0 + wave_m * WM + i * 32 + sub * 16 + qr;
-          const floatx4_t* src = reinterpret_cast<const floatx4_t*>(fs + qr * 64 + 16 * qb);
+          const floatx4_t* src = reinterpret_cast<const floatx4_t*>(fs + (sub * 16 + qr) * 64 + 16 * qb);
           float vals[16];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -714,7 +713,6 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
 #pragma unroll
             for (int t = 0; t < 4; ++t) vals[4 * e + t] = f4[t];
           }
-          __asm__ volatile("" ::: "memory");  // reads done before the next strip is written
           if (row < M) {
             uint32_t w0, w1;
             const uint32_t sc = quantize_block(vals, hg, r6, w0, w1);
@@ -728,6 +726,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
             }
           }
         }
+        __asm__ volatile("" ::: "memory");  // reads done before the next block is written
+      }
     }
     return;
   }
