@@ -428,10 +428,13 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   constexpr int kLoadsPerStage = 12;                  // vector-memory instructions per wave per stage
   using out_t = typename std::conditional<kOutBf16, __bf16, float>::type;
   constexpr int kEsz = sizeof(out_t);
-  // output rows staged per pass: a whole 32-row block for bf16 output (every
-  // lane then writes in every pass), 16 for fp32 (LDS room)
-  constexpr int kStripRows = kOutBf16 ? 32 : 16;
-  constexpr int kStripRow = WN * kEsz + 16;           // staged row bytes (+16 against bank conflicts)
+  // Output staged per pass: a whole 32-row block (every lane then writes in
+  // every pass) by 256 bytes of each row: all 128 columns of the wave for
+  // bf16, half of them for fp32.
+  constexpr int kStripRows = 32;
+  constexpr int kColPasses = kOutBf16 ? 1 : 2;
+  constexpr int kStripCols = WN / kColPasses;
+  constexpr int kStripRow = kStripCols * kEsz + 16;   // staged row bytes (+16 against bank conflicts)
   constexpr int kStripBytes = kStripRows * kStripRow;
   static_assert(STAGES >= 3, "ring depth");
   static_assert((STAGES - 1) * kLoadsPerStage < 64, "vmcnt range");
@@ -670,8 +673,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   // Epilogue.  Lane (r32, half) of block (j, i) holds, for output row
   // m = m0 + 128 wave_m + 32 i + r32, the columns n0 + 128 wave_n + 32 j +
   // 8 (v / 4) + 4 half + (v % 4), v = 0..15: four consecutive columns per
-  // group of 4 accumulators.  Rows go through LDS in strips of 32 (bf16
-  // output) or 16 (fp32).  RN32(g_a g_w) of the wave's 128 columns goes to a
+  // group of 4 accumulators.  Rows go through LDS in strips of 32 rows by
+  // 256 bytes (128 bf16 or 64 fp32 columns).  RN32(g_a g_w) of the wave's 128 columns goes to a
   // small LDS table, from which each lane reads the scales of its 64
   // columns once.  When one column range covers all 128 columns (every plain
   // GEMM, and most tiles of a segmented one) the table is filled with one
@@ -790,9 +793,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   }
   {
     uint8_t* strip = smem + STAGES * kStageBytes + wave * kStripBytes;
-    constexpr int kChunksPerRow = WN * kEsz / 16;
+    constexpr int kChunksPerRow = kStripCols * kEsz / 16;
     constexpr int kChunkElems = 16 / kEsz;
-    constexpr int kSubs = 32 / kStripRows;  // passes per 32-row block
+    constexpr int kJPerPass = FN / kColPasses;
     // the lane's 64 column scales (4 per group of 4 columns), read once
     floatx4_t al[FN][4];
 #pragma unroll
@@ -802,30 +805,29 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int sub = 0; sub < kSubs; ++sub) {  // rows r32 in [kStripRows sub, kStripRows (sub + 1))
-        if (kSubs == 1 || (r32 >> 4) == sub) {
-          uint8_t* rowp = strip + (r32 % kStripRows) * kStripRow;
+      for (int jp = 0; jp < kColPasses; ++jp) {  // columns [kStripCols jp, kStripCols (jp + 1)) of the wave
+        uint8_t* rowp = strip + r32 * kStripRow;
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
+        for (int jl = 0; jl < kJPerPass; ++jl)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int col = j * 32 + g * 8 + half * 4;
-              if constexpr (kOutBf16) {
-                typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
-                bf4_t o;
+          for (int g = 0; g < 4; ++g) {
+            const int j = jp * kJPerPass + jl;
+            const int col = jl * 32 + g * 8 + half * 4;  // within the strip
+            if constexpr (kOutBf16) {
+              typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
+              bf4_t o;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) o[t] = (__bf16)(acc[j][i][4 * g + t] * al[j][g][t]);
-                *reinterpret_cast<bf4_t*>(rowp + col * kEsz) = o;
-              } else {
-                floatx4_t o;
+              for (int t = 0; t < 4; ++t) o[t] = (__bf16)(acc[j][i][4 * g + t] * al[j][g][t]);
+              *reinterpret_cast<bf4_t*>(rowp + col * kEsz) = o;
+            } else {
+              floatx4_t o;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) o[t] = acc[j][i][4 * g + t] * al[j][g][t];
-                *reinterpret_cast<floatx4_t*>(rowp + col * kEsz) = o;
-              }
+              for (int t = 0; t < 4; ++t) o[t] = acc[j][i][4 * g + t] * al[j][g][t];
+              *reinterpret_cast<floatx4_t*>(rowp + col * kEsz) = o;
             }
-        }
-        const int grow0 = m0 + wave_m * WM + i * 32 + sub * kStripRows;
-        const int gcol0 = n0 + wave_n * WN;
+          }
+        const int grow0 = m0 + wave_m * WM + i * 32;
+        const int gcol0 = n0 + wave_n * WN + jp * kStripCols;
         constexpr int kQ = kStripRows * kChunksPerRow / 64;
         u32x4_t d[kQ];
 #pragma unroll
