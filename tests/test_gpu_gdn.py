@@ -201,3 +201,36 @@ def test_snapshot_steps_out_of_order_or_past_the_end_are_skipped():
         assert np.all(err <= e_S[t]), f"slot {slot} (token {t}): {err} > {e_S[t]}"
     for slot in (1, 3, 5):
         assert np.all(np.isnan(got[slot])), f"slot {slot} was written"
+
+
+@pytest.mark.parametrize("want_norms", [False, True])
+def test_recurrence_many_chunks_and_segments(want_norms):
+    # 9000 tokens: 141 chunks of 64 per-token scalars; snapshots inside,
+    # at and next to chunk edges restart the ring at unaligned tokens
+    print(f"[gdn] T=9000 norms={want_norms}", flush=True)
+    dev = need_gpu()
+    T = 9000
+    x = _rows(T, 31)
+    steps = (63, 64, 130, 4095, 8999)
+    so = torch.empty((4, D, D), dtype=torch.float32, device=dev)
+    o = torch.empty((T, 4 * D), dtype=torch.float32, device=dev)
+    nr = torch.empty((T, 4), dtype=torch.float32, device=dev) if want_norms else None
+    st = torch.tensor(steps, dtype=torch.int32, device=dev)
+    sn = torch.empty((len(steps), 4, D, D), dtype=torch.float32, device=dev)
+    nv.gdn_recurrence(torch.from_numpy(x).to(dev), **LAYOUT, n_qk_heads=2, n_v_heads=4, state_out=so, o=o,
+                      state_norms=nr, snap_steps=st, snaps=sn)
+    torch.cuda.synchronize()
+    q, k, v, g, beta = G.split_projection_rows(x, **LAYOUT, n_qk=2, n_v=4)
+    O, S, SN, NR = G.gdn_recurrence_ref(q, k, v, g, beta, snap_steps=steps)
+    norm_S = np.sqrt(NR)
+    M = np.maximum.accumulate(norm_S + beta * np.linalg.norm(v, axis=2), axis=0)
+    e_S = np.arange(1, T + 1)[:, None] * (D + 16) * 2.0 ** -24 * M
+    err = np.linalg.norm((so.cpu().numpy() - S).reshape(4, -1), axis=1)
+    assert np.all(err <= e_S[-1]), f"state error {err} > {e_S[-1]}"
+    for i, s in enumerate(steps):
+        se = np.linalg.norm((sn[i].cpu().numpy() - SN[i]).reshape(4, -1), axis=1)
+        assert np.all(se <= e_S[s]), f"snapshot {s}: {se} > {e_S[s]}"
+    oe = np.linalg.norm(o.cpu().numpy().reshape(T, 4, D) - O, axis=2)
+    assert np.all(oe <= (e_S + D * 2.0 ** -24 * norm_S) / np.sqrt(D))
+    if want_norms:
+        assert np.all(np.abs(np.sqrt(nr.cpu().numpy()) - norm_S) <= e_S + 1e-30)
