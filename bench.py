@@ -314,7 +314,10 @@ def main():
             torch.cuda.synchronize()
         t_sus = (t_sus0, time.time())
 
-    # practical HBM ceiling next to the spec figure: a plain 1 GiB device copy
+    # a plain 1 GiB device copy (torch copy_, one byte written per byte read)
+    # timed beside the spec figure.  The quantizer reads 2 B and writes
+    # 0.5625 B per value, a mix HBM serves faster than a 1:1 copy, so this is
+    # a reference point, not a ceiling for it.
     copy_gbps = None
     try:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
@@ -331,8 +334,8 @@ def main():
     except Exception:  # noqa: BLE001  (report, never fail the bench on this extra)
         copy_gbps = None
     if copy_gbps:
-        roofline_q["practical_peak_copy_gbps"] = round(copy_gbps, 1)
-        roofline_q["frac_of_practical_peak"] = round(q_ach / copy_gbps, 4)
+        roofline_q["torch_copy_1gib_gbps"] = round(copy_gbps, 1)
+        roofline_q["ratio_to_torch_copy"] = round(q_ach / copy_gbps, 4)
 
     # amax mode (dynamic activation scale) costs one more read of X
     amax_ms = None
