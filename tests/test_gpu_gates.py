@@ -13,7 +13,7 @@ import torch
 
 import nvfp4_w4a4_quantized_05_amd as nv
 from oracle import nvfp4_ref as ref
-from tests.gpu_util import GEMM_RTOL, host_f32, need_gpu
+from tests.gpu_util import GEMM_RTOL, assert_gemm_close, host_f32, need_gpu
 from workloads import activations, normal_weights
 
 pytestmark = pytest.mark.gpu
@@ -47,7 +47,8 @@ def _case(M, K, rows, decay, write, seed, rows_sample=None):
         if m >= 0:
             gate_cols[starts[m]:starts[m + 1]] = True
     sample = np.arange(M) if rows_sample is None else rows_sample
-    ah = (a[0].cpu().numpy()[sample], a[1].cpu().numpy()[sample], np.float32(a[2].item()))
+    sample_t = torch.from_numpy(sample).to(dev)
+    ah = (a[0][sample_t].cpu().numpy(), a[1][sample_t].cpu().numpy(), np.float32(a[2].item()))
     G, Y, S = ref.gemm_segmented_gates_ref(*ah, wc.cpu().numpy(), wsc.cpu().numpy(), mgs.cpu().numpy(), rows,
                                            decay, a_log, dt_bias, write)
     for od in (torch.float32, torch.bfloat16):
@@ -56,7 +57,11 @@ def _case(M, K, rows, decay, write, seed, rows_sample=None):
         torch.cuda.synchronize()
         assert torch.equal(y[:, ~torch.from_numpy(gate_cols).to(dev)], y0[:, ~torch.from_numpy(gate_cols).to(dev)]), \
             f"non-gate columns differ from nvfp4_gemm_segmented ({od})"
-        yv = host_f32(y)[sample].astype(np.float64)
+        # the segmented epilogue itself, on the columns without a gate
+        assert_gemm_close(y0[sample_t][:, torch.from_numpy(~gate_cols).to(dev)], Y[:, ~gate_cols], S[:, ~gate_cols],
+                          f"segmented epilogue ({od})")
+        yv = host_f32(y[sample_t]).astype(np.float64)
+        del y0
         tol = np.zeros_like(G)
         if decay >= 0:
             sl = slice(starts[decay], starts[decay + 1])
@@ -100,3 +105,11 @@ def test_gates_fused_gdn_in_projection():
     # the fused GDN in-projection (qkv 8192 | z 4096 | a 48 | b 48) at 4096 tokens
     print("[gates] fused GDN in-projection 4096 x 12384 x 5120", flush=True)
     _case(4096, 5120, [8192, 4096, 48, 48], 2, 3, seed=6, rows_sample=np.array([0, 513, 2048, 4095]))
+
+
+def test_gates_fused_gdn_in_projection_32k_tokens():
+    # the same projection at 32768 tokens with bf16 and fp32 output: the
+    # launch the bench times (128 x 49 big tiles)
+    print("[gates] fused GDN in-projection 32768 x 12384 x 5120", flush=True)
+    _case(32768, 5120, [8192, 4096, 48, 48], 2, 3, seed=8,
+          rows_sample=np.array([0, 255, 256, 16383, 20000, 32767]))

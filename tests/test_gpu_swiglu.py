@@ -21,8 +21,10 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("M,F,K,sample", [(300, 192, 256, None), (257, 64, 128, None), (1000, 512, 1024, None),
-                                          (4096, 17408, 5120, (0, 1, 255, 2049, 4095))])
+                                          (4096, 17408, 5120, (0, 1, 255, 2049, 4095)),
+                                          (32768, 17408, 5120, (0, 255, 256, 16383, 32767))])
 def test_swiglu_quantize_epilogue(M, F, K, sample):
+    # the last shape is the MLP of a 32768-token layer, the launch the bench times
     dev = need_gpu()
     print(f"[swiglu] M={M} F={F} K={K}", flush=True)
     x = activations("t3_outlier1pct", M, K, seed=M + F, device=dev)
@@ -32,20 +34,25 @@ def test_swiglu_quantize_epilogue(M, F, K, sample):
     nv.gemm_swiglu_quantize(*a, *w, torch.ones(1, device=dev), h=h)               # h for calibration
     hg = nv.quantize(h[:, :F].contiguous())[2].clone()                            # amax / 2688
     codes, scales, _ = nv.gemm_swiglu_quantize(*a, *w, hg, h=h)
+    codes_only = nv.gemm_swiglu_quantize(*a, *w, hg)                               # no h: the chain's form
     torch.cuda.synchronize()
+    assert torch.equal(codes_only[0], codes) and torch.equal(codes_only[1], scales), "codes depend on h"
+    del codes_only
     assert torch.isnan(h[:, F:]).all(), "h written past column F"
     hv = h[:, :F].contiguous()
+    del h
     c2, s2, _ = nv.quantize(hv, hg, from_amax=False)
     torch.cuda.synchronize()
     assert_codes_equal(codes, scales, c2.cpu().numpy(), s2.cpu().numpy(), "fused vs nvfp4_quantize of h")
     rows = np.arange(M) if sample is None else np.array(sample)
-    ah = (a[0].cpu().numpy()[rows], a[1].cpu().numpy()[rows], np.float32(a[2].item()))
+    rows_t = torch.from_numpy(rows).to(dev)
+    ah = (a[0][rows_t].cpu().numpy(), a[1][rows_t].cpu().numpy(), np.float32(a[2].item()))
     wh = (w[0].cpu().numpy(), w[1].cpu().numpy(), np.float32(w[2].item()))
     H, G, U, SG, SU = ref.gemm_swiglu_ref(*ah, *wh)
     eg, eu = GEMM_RTOL * SG, GEMM_RTOL * SU
     # plus the fp32 evaluation: a few ulp, and |g| 2^-23 relative from the exp2 argument's rounding
     tol = 1.1 * (np.abs(U) + eu) * eg + (np.abs(ref.silu(G)) + 1.1 * eg) * eu + \
         (2.0 ** -20 + np.abs(G) * 2.0 ** -22) * np.abs(H) + 1e-30
-    err = np.abs(host_f32(hv)[rows].astype(np.float64) - H)
+    err = np.abs(host_f32(hv[rows_t]).astype(np.float64) - H)
     bad = np.argwhere(err > tol)
     assert bad.size == 0, f"{len(bad)} h values out of tolerance, first {bad[:3].tolist()}"
