@@ -31,10 +31,13 @@ def _case(M, rows, K, seed, mults):
 # (M, module rows, K): decode kernel (M <= 64, K % 256 == 0; workgroups of
 # 16, 32 and 64 weight rows), generic kernel (K % 128 != 0), streaming kernel
 # (>= 256 tiles of 256 x 256); boundaries fall inside workgroup tiles, one
-# module is empty.
+# module is empty.  The fused GDN in-projection (8192 | 4096 | 48 | 48 rows,
+# K = 5120) at 1 and 64 rows is the decode step the bench times.
 SHAPES = [
     (5, (40, 0, 17, 7), 512),
     (3, (8192, 4096, 48, 48), 512),
+    (1, (8192, 4096, 48, 48), 5120),
+    (64, (8192, 4096, 48, 48), 5120),
     (20, (2000, 3000, 120), 256),
     (64, (8192 // 64, 48, 48, 300), 1024),
     (37, (100, 3, 60), 144),
