@@ -161,3 +161,31 @@ def test_deterministic_repeat():
     y2 = nv.gemm(*a, *b)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+def test_operands_past_2gib_take_64bit_offsets():
+    """A [262181 x 16384]: 4.3 G values (past 2^32 elements in the quantizer)
+    and 2.15 GB of codes (past 2^31 bytes, so the GEMM takes the generic
+    kernel, whose offsets are 64-bit).  The tensor scale is given, so sampled
+    rows on both sides of the 2 GiB mark can be checked against the oracle."""
+    dev = need_gpu()
+    M, N, K = 262181, 200, 16384
+    assert M * (K // 2) > 2 ** 31 and M * K > 2 ** 32
+    print(f"[gemm] past 2 GiB: A {M}x{K} bf16, W {N}x{K}", flush=True)
+    gen = torch.Generator(device=dev).manual_seed(77)
+    x = torch.randn((M, K), generator=gen, device=dev, dtype=torch.bfloat16)
+    g = np.float32(0.0025)
+    a = nv.quantize(x, torch.tensor([g], device=dev), from_amax=False)
+    w = normal_weights(N, K, 0.02, seed=78, device=dev)
+    b = nv.quantize(w)
+    y = nv.gemm(*a, *b, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = np.array([0, 131071, 262143, 262144, 262145, M - 1])   # 262144 * 8192 = 2^31
+    rows_t = torch.from_numpy(rows).to(dev)
+    oa = ref.quantize(host_f32(x[rows_t]), g=g)
+    assert np.array_equal(a[0][rows_t].cpu().numpy(), oa[0]) and np.array_equal(a[1][rows_t].cpu().numpy(), oa[1])
+    ow = ref.quantize(host_f32(w))
+    assert np.array_equal(b[0].cpu().numpy(), ow[0]) and np.array_equal(b[1].cpu().numpy(), ow[1])
+    assert float(b[2].item()) == float(ow[2])
+    Y, S = ref.gemm_ref(*oa, *ow)
+    assert_gemm_close(y[rows_t], Y, S, "A past 2 GiB")
