@@ -189,3 +189,48 @@ def test_operands_past_2gib_take_64bit_offsets():
     assert float(b[2].item()) == float(ow[2])
     Y, S = ref.gemm_ref(*oa, *ow)
     assert_gemm_close(y[rows_t], Y, S, "A past 2 GiB")
+
+
+def test_streaming_and_decode_kernels_just_below_their_offset_limits():
+    """The large-tile and decode kernels address their operands with 32-bit
+    buffer offsets and are taken only below 2^31 bytes: A of 262143 x 16384
+    (2^31 - 8 KiB of codes) through the large-tile kernel, and W of 262079
+    rows x 16384 through the decode kernel, checked on the last rows and
+    columns.  Tensor scales are given, so the oracle needs only the samples."""
+    dev = need_gpu()
+    K = 16384
+    g = torch.tensor([0.0025], device=dev)
+    gen = torch.Generator(device=dev).manual_seed(91)
+    # large-tile kernel: M x K/2 = 2^31 - 8192, N = 256 (1024 tiles of 256 x 256)
+    M, N = 262143, 256
+    print(f"[gemm] large-tile kernel at its limit: A {M}x{K}, W {N}x{K}", flush=True)
+    x = torch.randn((M, K), generator=gen, device=dev, dtype=torch.bfloat16)
+    a = nv.quantize(x, g, from_amax=False)
+    w = normal_weights(N, K, 0.02, seed=92, device=dev)
+    b = nv.quantize(w)
+    y = nv.gemm(*a, *b, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = np.array([0, 131072, M - 256, M - 2, M - 1])
+    rows_t = torch.from_numpy(rows).to(dev)
+    oa = ref.quantize(host_f32(x[rows_t]), g=np.float32(0.0025))
+    ow = ref.quantize(host_f32(w))
+    Y, S = ref.gemm_ref(*oa, *ow)
+    assert_gemm_close(y[rows_t], Y, S, "large-tile kernel, last rows")
+    del x, a, y
+    # decode kernel: (N + 64) x K/2 = 2^31 - 8192, M = 3
+    M, N = 3, 262079
+    print(f"[gemm] decode kernel at its limit: A {M}x{K}, W {N}x{K}", flush=True)
+    x = torch.randn((M, K), generator=gen, device=dev, dtype=torch.bfloat16)
+    a = nv.quantize(x)
+    w = torch.randn((N, K), generator=gen, device=dev, dtype=torch.bfloat16)
+    b = nv.quantize(w, g, from_amax=False)
+    y = nv.gemm(*a, *b, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    cols = np.array([0, 131040, N - 64, N - 2, N - 1])
+    cols_t = torch.from_numpy(cols).to(dev)
+    oa = ref.quantize(host_f32(x))
+    assert float(a[2].item()) == float(oa[2])
+    ow = ref.quantize(host_f32(w[cols_t]), g=np.float32(0.0025))
+    assert np.array_equal(b[0][cols_t].cpu().numpy(), ow[0]) and np.array_equal(b[1][cols_t].cpu().numpy(), ow[1])
+    Y, S = ref.gemm_ref(*oa, *ow)
+    assert_gemm_close(y[:, cols_t], Y, S, "decode kernel, last weight rows")
