@@ -91,7 +91,9 @@ typedef enum { NVFP4_SCALE_GIVEN = 0, NVFP4_SCALE_FROM_AMAX = 1 } nvfp4_scale_mo
  *   mode         nvfp4_scale_mode_t
  *   stream       hipStream_t or NULL
  * FROM_AMAX enqueues four kernels (clear, absolute-max reduction, encode,
- * finalize); GIVEN enqueues one.  Output is deterministic.
+ * finalize); GIVEN enqueues one.  Output is deterministic.  rows == 0:
+ * nothing is encoded (x, codes and scales may be NULL); FROM_AMAX still
+ * writes g = 1.0, the amax of no values being 0, and GIVEN enqueues nothing.
  */
 NVFP4_API nvfp4_status_t nvfp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t cols,
                               int64_t ldx, uint8_t* codes, uint8_t* scales,

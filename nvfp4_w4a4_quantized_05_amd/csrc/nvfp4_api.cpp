@@ -53,7 +53,13 @@ nvfp4_status_t nvfp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int
     if (mode != NVFP4_SCALE_GIVEN && mode != NVFP4_SCALE_FROM_AMAX) return NVFP4_ERR_MODE;
     if (rows < 0 || cols <= 0 || cols % 16 != 0 || ldx < cols) return NVFP4_ERR_SHAPE;
     if (rows > INT64_MAX / (ldx > 0 ? ldx : 1) / 4) return NVFP4_ERR_SHAPE;
-    if (rows == 0) return NVFP4_OK;
+    if (rows == 0) {  // nothing to encode; FROM_AMAX still writes g (1.0: no values, amax 0)
+      if (mode == NVFP4_SCALE_GIVEN) return NVFP4_OK;
+      if (!global_scale) return NVFP4_ERR_NULL;
+      if (!aligned(global_scale, 4)) return NVFP4_ERR_ALIGN;
+      return hip_status(nvfp4::launch_quantize(nullptr, in_dtype == NVFP4_IN_BF16, 0, cols, ldx, nullptr, nullptr,
+                                               global_scale, true, (hipStream_t)stream));
+    }
     if (!x || !codes || !scales || !global_scale) return NVFP4_ERR_NULL;
     const int64_t esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
     if (!aligned(x, 16) || (ldx * esize) % 16 != 0 || !aligned(codes, 8) || !aligned(global_scale, 4))

@@ -131,18 +131,20 @@ hipError_t launch_typed(const void* x, int64_t rows, int64_t cols, int64_t ldx, 
   const int64_t nblocks = rows * bpr;
   if (from_amax) {
     clear_word_kernel<<<1, 1, 0, stream>>>(reinterpret_cast<uint32_t*>(gs));
-    const int per = kBf16 ? 8 : 4;
-    const int64_t cpr = cols / per;
-    const int64_t nchunks = rows * cpr;
-    int64_t grid = (nchunks + kThreads * 4 - 1) / (kThreads * 4);
-    if (grid > 256 * 16) grid = 256 * 16;
-    if (grid < 1) grid = 1;
-    amax_kernel<kBf16, kContig><<<(unsigned)grid, kThreads, 0, stream>>>(
-        x, nchunks, cpr, ldx, reinterpret_cast<uint32_t*>(gs));
-    quantize_kernel<kBf16, kContig, 1><<<(unsigned)((nblocks + kThreads - 1) / kThreads), kThreads, 0,
-                                         stream>>>(x, nblocks, bpr, ldx, codes, scales, gs);
+    if (nblocks > 0) {  // no rows: the amax of no values is 0, so g = 1.0
+      const int per = kBf16 ? 8 : 4;
+      const int64_t cpr = cols / per;
+      const int64_t nchunks = rows * cpr;
+      int64_t grid = (nchunks + kThreads * 4 - 1) / (kThreads * 4);
+      if (grid > 256 * 16) grid = 256 * 16;
+      if (grid < 1) grid = 1;
+      amax_kernel<kBf16, kContig><<<(unsigned)grid, kThreads, 0, stream>>>(
+          x, nchunks, cpr, ldx, reinterpret_cast<uint32_t*>(gs));
+      quantize_kernel<kBf16, kContig, 1><<<(unsigned)((nblocks + kThreads - 1) / kThreads), kThreads, 0,
+                                           stream>>>(x, nblocks, bpr, ldx, codes, scales, gs);
+    }
     finalize_scale_kernel<<<1, 1, 0, stream>>>(gs);
-  } else {
+  } else if (nblocks > 0) {
     quantize_kernel<kBf16, kContig, 0><<<(unsigned)((nblocks + kThreads - 1) / kThreads), kThreads, 0,
                                          stream>>>(x, nblocks, bpr, ldx, codes, scales, gs);
   }

@@ -69,6 +69,9 @@ def test_quantize_rejects_bad_arguments(lib):
     assert q(lib, ldx=36) == ALIGN            # bf16 row stride of 72 bytes
     assert q(lib, codes=ctypes.c_void_p(0x10004)) == ALIGN
     assert q(lib, rows=0, x=None, codes=None, scales=None, gs=None) == OK   # empty: no-op
+    # empty with the scale from amax: g = 1.0 is still written, so it must be valid
+    assert q(lib, rows=0, x=None, codes=None, scales=None, gs=None, mode=1) == NULL
+    assert q(lib, rows=0, x=None, codes=None, scales=None, gs=P_ODD, mode=1) == ALIGN
     assert lib.nvfp4_last_hip_error() == 0
 
 

@@ -231,3 +231,20 @@ def test_config_weights_full(name):
         wc, ws, wg = ref.quantize(w.numpy())
         assert gs.item() == float(wg)
         assert_codes_equal(c, s, wc, ws, f"{name} weight {p.name}")
+
+
+def test_zero_rows():
+    """No rows: nothing is encoded; the amax mode still writes the tensor scale
+    of an all-zero input, 1.0 (the oracle's value for a tensor with no values)."""
+    dev = need_gpu()
+    print("[quantize] zero rows", flush=True)
+    for dtype in (torch.bfloat16, torch.float32):
+        x = torch.empty((0, 256), dtype=dtype, device=dev)
+        g = torch.full((1,), float("nan"), dtype=torch.float32, device=dev)
+        c, s, g = nv.quantize(x, g, from_amax=True)
+        torch.cuda.synchronize()
+        assert c.shape == (0, 128) and s.shape == (0, 16)
+        assert float(g.item()) == float(ref.global_scale(np.zeros((0, 256), np.float32))) == 1.0
+        c, s, g2 = nv.quantize(x, torch.tensor([0.5], device=dev), from_amax=False)
+        torch.cuda.synchronize()
+        assert float(g2.item()) == 0.5
