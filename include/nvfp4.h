@@ -254,7 +254,8 @@ NVFP4_API nvfp4_status_t nvfp4_gemm_swiglu_quantize(const uint8_t* a_codes, cons
  *               n_v_heads <= 65535
  *   state_in    device [n_v_heads x 128 x 128] fp32 (i = d_k row major), or
  *               NULL for zeros (read)
- *   state_out   device, same layout, or NULL: S_T (written)
+ *   state_out   device, same layout, or NULL: S_T (written; with T = 0 the
+ *               start state, zeros without state_in)
  *   o           device [T x ldo] fp32, head h at columns 128 h, or NULL
  *   state_norms device [T x n_v_heads] fp32 or NULL: |S_t|_F^2 per head
  *   snap_steps, n_snaps, snaps   device: n_snaps strictly increasing token
@@ -266,10 +267,12 @@ NVFP4_API nvfp4_status_t nvfp4_gemm_swiglu_quantize(const uint8_t* a_codes, cons
  * aligned (NVFP4_ERR_ALIGN).  The columns of each state are independent and
  * are split over workgroups (8 per value head; one per head when
  * state_norms is asked for), each running the tokens in order; the per-token
- * sums are fixed-order, so results are reproducible.  Accuracy: the update
- * operator has norm <= 1, so rounding errors
- * add without growing: |S_t - S_t(exact)|_F <= t (128 + 16) 2^-24 max_s<=t
- * (|S_s|_F + beta_s |v_s|).
+ * sums are fixed-order, so results are reproducible.  Accuracy: a token
+ * adds at most (128 + 16) 2^-24 M_t of rounding error, M_t = max over s <= t
+ * of |S_s|_F + beta_s |v_s|, and the update carries the earlier error
+ * through alpha I - beta khat khat^T, of spectral norm c_t = max(alpha_t,
+ * |alpha_t - beta_t|) <= 1: e_t <= c_t e_{t-1} + (128 + 16) 2^-24 M_t, at most
+ * t (128 + 16) 2^-24 M_t.
  */
 NVFP4_API nvfp4_status_t nvfp4_gdn_recurrence(const float* x, int64_t ldx, int64_t q_col, int64_t k_col,
                                               int64_t v_col, int64_t g_col, int64_t beta_col, int64_t T,

@@ -170,7 +170,11 @@ nvfp4_status_t nvfp4_gdn_recurrence(const float* x, int64_t ldx, int64_t q_col, 
     if (g_col < 0 || g_col + n_v_heads > ldx || beta_col < 0 || beta_col + n_v_heads > ldx) return NVFP4_ERR_SHAPE;
     if (o && ldo < n_v_heads * kD) return NVFP4_ERR_SHAPE;
     if (n_snaps < 0) return NVFP4_ERR_SHAPE;
-    if (T == 0) return NVFP4_OK;
+    if (T == 0) {  // S_0 is the start state; nothing else has a row to write
+      if (!state_out) return NVFP4_OK;
+      if (!aligned(state_out, 4) || (state_in && !aligned(state_in, 4))) return NVFP4_ERR_ALIGN;
+      return hip_status(nvfp4::launch_gdn_start_state(state_in, state_out, n_v_heads, (hipStream_t)stream));
+    }
     if (!x || (n_snaps > 0 && (!snap_steps || !snaps))) return NVFP4_ERR_NULL;
     for (const void* p : {(const void*)x, (const void*)state_in, (const void*)state_out, (const void*)o,
                           (const void*)state_norms, (const void*)snap_steps, (const void*)snaps})

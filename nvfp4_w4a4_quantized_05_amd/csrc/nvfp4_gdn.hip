@@ -382,7 +382,20 @@ hipError_t launch_variant(bool vec, const float* x, int64_t ldx, int64_t q_col, 
   return hipGetLastError();
 }
 
+// S_0 = the start state (zeros without one), element by element; in and
+// out may be the same buffer.
+__global__ void gdn_start_state_kernel(const float* in, float* out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = in ? in[i] : 0.0f;
+}
+
 }  // namespace
+
+hipError_t launch_gdn_start_state(const float* s_in, float* s_out, int n_v, hipStream_t stream) {
+  const int64_t n = (int64_t)n_v * kD * kD;
+  gdn_start_state_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(s_in, s_out, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_gdn_recurrence(const float* x, int64_t ldx, int64_t q_col, int64_t k_col, int64_t v_col,
                                  int64_t g_col, int64_t b_col, int64_t T, int n_qk, int n_v, const float* s_in,

@@ -66,11 +66,16 @@ hipError_t launch_harmonize(uint8_t* scales, const float* module_gs, const int64
                             int32_t n_modules, int64_t K, float* shared_gs, uint32_t* counters,
                             hipStream_t stream);
 
-// Gated DeltaNet recurrence over T tokens, one workgroup per value head
-// (head dimension 128); arguments as nvfp4_gdn_recurrence, already checked.
+// Gated DeltaNet recurrence over T >= 1 tokens, the columns of each value
+// head's state (head dimension 128) split over workgroups; arguments as
+// nvfp4_gdn_recurrence, already checked.
 hipError_t launch_gdn_recurrence(const float* x, int64_t ldx, int64_t q_col, int64_t k_col, int64_t v_col,
                                  int64_t g_col, int64_t b_col, int64_t T, int n_qk, int n_v, const float* s_in,
                                  float* s_out, float* o, int64_t ldo, float* norms, const int* snap_steps,
                                  int n_snaps, float* snaps, hipStream_t stream);
+
+// S_0 of a recurrence over no tokens: s_out = s_in, or zeros when s_in is
+// NULL ([n_v x 128 x 128] fp32; s_in may equal s_out).
+hipError_t launch_gdn_start_state(const float* s_in, float* s_out, int n_v, hipStream_t stream);
 
 }  // namespace nvfp4

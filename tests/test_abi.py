@@ -211,8 +211,8 @@ def test_binding_refuses_cpu_tensors():
 
 
 def gd(lib, x=P16, ldx=1040, cols=(0, 256, 512, 1024, 1028), T=8, nqk=2, nv_=4, o=None, ldo=0, n_snaps=0,
-       steps=None, snaps=None, s_in=None):
-    return lib.nvfp4_gdn_recurrence(x, ldx, *cols, T, nqk, nv_, s_in, None, o, ldo, None, steps, n_snaps, snaps,
+       steps=None, snaps=None, s_in=None, s_out=None):
+    return lib.nvfp4_gdn_recurrence(x, ldx, *cols, T, nqk, nv_, s_in, s_out, o, ldo, None, steps, n_snaps, snaps,
                                     None)
 
 
@@ -231,6 +231,7 @@ def test_gdn_recurrence_rejects_bad_arguments(lib):
     assert gd(lib, x=ctypes.c_void_p(0x10002)) == ALIGN
     assert gd(lib, s_in=ctypes.c_void_p(0x10002)) == ALIGN
     assert gd(lib, T=0, x=None) == OK                        # nothing to do
+    assert gd(lib, T=0, x=None, s_out=P_ODD) == ALIGN        # S_0 would be written there
     assert gd(lib, T=0, cols=(0, 256, -1, 1024, 1028)) == OK  # v = 0 is allowed
     assert lib.nvfp4_last_hip_error() == 0
 

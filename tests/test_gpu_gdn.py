@@ -123,7 +123,17 @@ def test_single_token_and_empty():
     _check(_rows(1, 5), snaps=(0,))
     dev = need_gpu()
     nv.gdn_recurrence(torch.zeros((0, LDX), dtype=torch.float32, device=dev), **LAYOUT, n_qk_heads=2, n_v_heads=4)
+    # no tokens: S_0 is the start state, or zeros without one
+    s0 = torch.randn((4, D, D), dtype=torch.float32, device=dev)
+    so = torch.full((4, D, D), np.nan, dtype=torch.float32, device=dev)
+    nv.gdn_recurrence(torch.zeros((0, LDX), dtype=torch.float32, device=dev), **LAYOUT, n_qk_heads=2, n_v_heads=4,
+                      state_in=s0, state_out=so)
     torch.cuda.synchronize()
+    assert torch.equal(so, s0)
+    nv.gdn_recurrence(torch.zeros((0, LDX), dtype=torch.float32, device=dev), **LAYOUT, n_qk_heads=2, n_v_heads=4,
+                      state_out=so)
+    torch.cuda.synchronize()
+    assert torch.equal(so, torch.zeros_like(so))
 
 
 def _check_heads(T, n_qk, n_v, seed):
