@@ -101,6 +101,41 @@ def _need_gpu(*ts):
             raise ValueError("nvfp4 calls take GPU tensors only")
 
 
+def _u8_matrix(t, shape, what):
+    """t must be a contiguous uint8 tensor of exactly `shape`."""
+    if t.dtype != torch.uint8 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous uint8 {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
+def _f32_scalars(t, n, what):
+    """t must hold at least n contiguous float32 values (tensor scales)."""
+    if t.dtype != torch.float32 or t.numel() < n or not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous float32 with {n} value(s)")
+
+
+def _out_matrix(out, M, N, out_dtype):
+    """out: 2-D, out_dtype, M rows, at least N columns, unit column stride."""
+    if out.dtype != out_dtype or out.dim() != 2 or out.stride(1) != 1:
+        raise ValueError("out must be 2-D with unit column stride and dtype out_dtype")
+    if out.shape[0] != M or out.shape[1] < N:
+        raise ValueError(f"out must be [{M}, >= {N}], got {tuple(out.shape)}")
+
+
+def _operands(a_codes, a_scales, a_gs, w_codes, w_scales, k):
+    """Shapes of the two NVFP4 operands; returns (M, N, K)."""
+    M = a_codes.shape[0]
+    N = w_codes.shape[0]
+    K = a_codes.shape[1] * 2 if k is None else k
+    if a_codes.dim() != 2 or w_codes.dim() != 2 or K <= 0 or K % 16:
+        raise ValueError("codes must be 2-D and K a positive multiple of 16")
+    _u8_matrix(a_codes, (M, K // 2), "a_codes")
+    _u8_matrix(a_scales, (M, K // 16), "a_scales")
+    _u8_matrix(w_codes, (N, K // 2), "w_codes")
+    _u8_matrix(w_scales, (N, K // 16), "w_scales")
+    _f32_scalars(a_gs, 1, "a_gs")
+    return M, N, K
+
+
 def quantize(x: torch.Tensor, global_scale: torch.Tensor | None = None, *, from_amax: bool | None = None,
              codes: torch.Tensor | None = None, scales: torch.Tensor | None = None, stream=None):
     """NVFP4-encode a 2-D bf16 or fp32 GPU tensor (rows contiguous, any row stride).
@@ -109,7 +144,6 @@ def quantize(x: torch.Tensor, global_scale: torch.Tensor | None = None, *, from_
     (calibrated scale), written with RN32(amax/2688) when ``from_amax``
     (default: from_amax = global_scale is None).  Returns (codes, scales, gs).
     """
-    _need_gpu(x, global_scale, codes, scales)
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     if x.dtype == torch.bfloat16:
@@ -119,6 +153,15 @@ def quantize(x: torch.Tensor, global_scale: torch.Tensor | None = None, *, from_
     else:
         raise ValueError(f"unsupported input dtype {x.dtype}")
     rows, cols = x.shape
+    if cols % 16:
+        raise ValueError("columns must be a multiple of 16")
+    if codes is not None:
+        _u8_matrix(codes, (rows, cols // 2), "codes")
+    if scales is not None:
+        _u8_matrix(scales, (rows, cols // 16), "scales")
+    if global_scale is not None:
+        _f32_scalars(global_scale, 1, "global_scale")
+    _need_gpu(x, global_scale, codes, scales)
     if from_amax is None:
         from_amax = global_scale is None
     if global_scale is None:
@@ -137,20 +180,14 @@ def quantize(x: torch.Tensor, global_scale: torch.Tensor | None = None, *, from_
 def gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, *, out_dtype=torch.float32,
          out: torch.Tensor | None = None, k: int | None = None, stream=None):
     """y[M, N] = RN32(g_a g_w) deq(A) deq(W)^T from NVFP4 A [M, K] and W [N, K]."""
-    _need_gpu(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, out)
-    M = a_codes.shape[0]
-    N = w_codes.shape[0]
-    K = a_codes.shape[1] * 2 if k is None else k
-    if w_codes.shape[1] * 2 != K or a_scales.shape != (M, K // 16) or w_scales.shape != (N, K // 16):
-        raise ValueError("operand shapes disagree")
-    for t in (a_codes, a_scales, w_codes, w_scales):
-        if not t.is_contiguous() or t.dtype != torch.uint8:
-            raise ValueError("codes and scales must be contiguous uint8")
+    M, N, K = _operands(a_codes, a_scales, a_gs, w_codes, w_scales, k)
+    _f32_scalars(w_gs, 1, "w_gs")
     od = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[out_dtype]
+    if out is not None:
+        _out_matrix(out, M, N, out_dtype)
+    _need_gpu(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, out)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
-    if out.dtype != out_dtype or out.stride(1) != 1:
-        raise ValueError("out must have unit column stride and dtype out_dtype")
     lib = load()
     ws_bytes = lib.nvfp4_gemm_workspace_size(M, N, K, od)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a_codes.device) if ws_bytes else None
@@ -165,23 +202,16 @@ def gemm_segmented(a_codes, a_scales, a_gs, w_codes, w_scales, module_gs, module
                    out_dtype=torch.float32, out: torch.Tensor | None = None, k: int | None = None, stream=None):
     """One GEMM over modules concatenated along N (module_rows rows each): the
     columns of module i are RN32(g_a g_i) deq(A) deq(W_i)^T, g_i = module_gs[i]."""
-    _need_gpu(a_codes, a_scales, a_gs, w_codes, w_scales, module_gs, out)
     rows = [int(r) for r in module_rows]
-    M = a_codes.shape[0]
-    N = w_codes.shape[0]
-    K = a_codes.shape[1] * 2 if k is None else k
+    M, N, K = _operands(a_codes, a_scales, a_gs, w_codes, w_scales, k)
     if sum(rows) != N or module_gs.numel() != len(rows) or module_gs.dtype != torch.float32:
         raise ValueError("module_rows must sum to the weight rows, one float32 scale per module")
-    if w_codes.shape[1] * 2 != K or a_scales.shape != (M, K // 16) or w_scales.shape != (N, K // 16):
-        raise ValueError("operand shapes disagree")
-    for t in (a_codes, a_scales, w_codes, w_scales):
-        if not t.is_contiguous() or t.dtype != torch.uint8:
-            raise ValueError("codes and scales must be contiguous uint8")
     od = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[out_dtype]
+    if out is not None:
+        _out_matrix(out, M, N, out_dtype)
+    _need_gpu(a_codes, a_scales, a_gs, w_codes, w_scales, module_gs, out)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
-    if out.dtype != out_dtype or out.stride(1) != 1:
-        raise ValueError("out must have unit column stride and dtype out_dtype")
     lib = load()
     ws_bytes = lib.nvfp4_gemm_workspace_size(M, N, K, od)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a_codes.device) if ws_bytes else None
@@ -200,27 +230,20 @@ def gemm_segmented_gates(a_codes, a_scales, a_gs, w_codes, w_scales, module_gs, 
     """gemm_segmented whose epilogue turns module `decay_module` into the decay
     gate -exp(a_log) softplus(v + dt_bias) and module `write_module` into
     sigmoid(v) (-1: none)."""
-    _need_gpu(a_codes, a_scales, a_gs, w_codes, w_scales, module_gs, a_log, dt_bias, out)
     rows = [int(r) for r in module_rows]
-    M = a_codes.shape[0]
-    N = w_codes.shape[0]
-    K = a_codes.shape[1] * 2
+    M, N, K = _operands(a_codes, a_scales, a_gs, w_codes, w_scales, None)
     if sum(rows) != N or module_gs.numel() != len(rows) or module_gs.dtype != torch.float32:
         raise ValueError("module_rows must sum to the weight rows, one float32 scale per module")
-    if w_codes.shape[1] * 2 != K or a_scales.shape != (M, K // 16) or w_scales.shape != (N, K // 16):
-        raise ValueError("operand shapes disagree")
-    for t in (a_codes, a_scales, w_codes, w_scales):
-        if not t.is_contiguous() or t.dtype != torch.uint8:
-            raise ValueError("codes and scales must be contiguous uint8")
     if decay_module >= 0:
         for t in (a_log, dt_bias):
             if t is None or t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != rows[decay_module]:
                 raise ValueError("a_log and dt_bias: contiguous float32, one per decay-module row")
     od = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[out_dtype]
+    if out is not None:
+        _out_matrix(out, M, N, out_dtype)
+    _need_gpu(a_codes, a_scales, a_gs, w_codes, w_scales, module_gs, a_log, dt_bias, out)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
-    if out.dtype != out_dtype or out.stride(1) != 1:
-        raise ValueError("out must have unit column stride and dtype out_dtype")
     lib = load()
     ws_bytes = lib.nvfp4_gemm_workspace_size(M, N, K, od)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a_codes.device) if ws_bytes else None
@@ -238,15 +261,13 @@ def gemm_swiglu_quantize(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, h_gs,
     """h = silu(gate) * up of the gate/up GEMM (W = [gate; up], 2F rows),
     quantized with tensor scale h_gs in the epilogue.  Returns (codes
     [M, F/2], scales [M, F/16], h_gs); h [M, >= F] fp32 is filled if given."""
+    M, N, K = _operands(a_codes, a_scales, a_gs, w_codes, w_scales, None)
+    if N % 2:
+        raise ValueError("the gate/up weight has 2F rows")
+    F = N // 2
+    _f32_scalars(w_gs, 1, "w_gs")
+    _f32_scalars(h_gs, 1, "h_gs")
     _need_gpu(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, h_gs, codes, scales, h)
-    M, K = a_codes.shape[0], a_codes.shape[1] * 2
-    if w_codes.shape[0] % 2 or w_codes.shape[1] * 2 != K or a_scales.shape != (M, K // 16) \
-            or w_scales.shape != (w_codes.shape[0], K // 16):
-        raise ValueError("operand shapes disagree")
-    F = w_codes.shape[0] // 2
-    for t in (a_codes, a_scales, w_codes, w_scales):
-        if not t.is_contiguous() or t.dtype != torch.uint8:
-            raise ValueError("codes and scales must be contiguous uint8")
     if codes is None:
         codes = torch.empty((M, F // 2), dtype=torch.uint8, device=a_codes.device)
     if scales is None:
@@ -303,22 +324,25 @@ def gdn_recurrence(x: torch.Tensor, *, q_col: int, k_col: int, v_col: int, g_col
 def quantize_gemm(x: torch.Tensor, a_gs: torch.Tensor, w_codes, w_scales, w_gs, *, out_dtype=torch.float32,
                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
     """y = gemm(quantize(x, a_gs), W) in one call (one kernel for decode-sized x)."""
-    _need_gpu(x, a_gs, w_codes, w_scales, w_gs, out, workspace)
     if x.dim() != 2 or x.stride(1) != 1 or x.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("x must be a 2-D bf16 or fp32 tensor with unit column stride")
     M, K = x.shape
     N = w_codes.shape[0]
-    if w_codes.shape[1] * 2 != K or w_scales.shape != (N, K // 16):
-        raise ValueError("operand shapes disagree")
-    for t in (w_codes, w_scales):
-        if not t.is_contiguous() or t.dtype != torch.uint8:
-            raise ValueError("codes and scales must be contiguous uint8")
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    _u8_matrix(w_codes, (N, K // 2), "w_codes")
+    _u8_matrix(w_scales, (N, K // 16), "w_scales")
+    _f32_scalars(a_gs, 1, "a_gs")
+    _f32_scalars(w_gs, 1, "w_gs")
     dt = IN_BF16 if x.dtype == torch.bfloat16 else IN_F32
     od = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[out_dtype]
+    if out is not None:
+        _out_matrix(out, M, N, out_dtype)
+    if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    _need_gpu(x, a_gs, w_codes, w_scales, w_gs, out, workspace)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    if out.dtype != out_dtype or out.stride(1) != 1:
-        raise ValueError("out must have unit column stride and dtype out_dtype")
     lib = load()
     ws_bytes = lib.nvfp4_quantize_gemm_workspace_size(M, N, K, dt, od)
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):

@@ -59,3 +59,51 @@ def assert_gemm_close(y: torch.Tensor, Y: np.ndarray, Sabs: np.ndarray, what="")
 
 def oracle_quantize(x: torch.Tensor, g=None):
     return ref.quantize(host_f32(x), g=g)
+
+
+def oracle_threads():
+    """Host threads for the oracle over big tensors (numpy releases the GIL in
+    its array loops): the host's share, at most 16."""
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def assert_quantize_matches_oracle_full(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, g,
+                                        what="", chunk_rows=512):
+    """Every code byte and scale byte of a GPU-quantized tensor against
+    ``ref.quantize`` of the same values with the same tensor scale g (the
+    quantizer is row-independent once g is fixed), in row chunks on host
+    threads.  x is the GPU input (bf16 or fp32); codes and scales are the GPU
+    results; g is the oracle's tensor scale (np.float32)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    rows = x.shape[0]
+    xh = x.detach().cpu()                                   # exact bf16 / fp32 values
+    ch, sh = codes.cpu().numpy(), scales.cpu().numpy()
+    g = np.float32(g)
+
+    def check(r0):
+        r1 = min(rows, r0 + chunk_rows)
+        oc, os_, _ = ref.quantize(xh[r0:r1].float().numpy(), g=g)
+        bad_s = np.argwhere(sh[r0:r1] != os_)
+        bad_c = np.argwhere(ch[r0:r1] != oc)
+        first = None
+        if bad_s.size:
+            i = tuple(bad_s[0])
+            first = f"scale [{r0 + i[0]}, {i[1]}] got {sh[r0 + i[0], i[1]]:#x} want {os_[i]:#x}"
+        elif bad_c.size:
+            i = tuple(bad_c[0])
+            first = f"code byte [{r0 + i[0]}, {i[1]}] got {ch[r0 + i[0], i[1]]:#04x} want {oc[i]:#04x}"
+        return len(bad_s), len(bad_c), first
+
+    with ThreadPoolExecutor(oracle_threads()) as ex:
+        res = list(ex.map(check, range(0, rows, chunk_rows)))
+    n_s = sum(r[0] for r in res)
+    n_c = sum(r[1] for r in res)
+    firsts = [r[2] for r in res if r[2]]
+    assert n_s == 0 and n_c == 0, f"{what}: {n_s} scale and {n_c} code-byte mismatches; first: {firsts[:1]}"
+    return codes.numel() + scales.numel()

@@ -258,3 +258,49 @@ def test_gemm_swiglu_quantize_rejects_bad_arguments(lib):
     assert sq(lib, h=P16, ldh=66) == ALIGN   # ldh % 4
     assert sq(lib, M=0, ptrs=[None] * 6, hgs=None, hc=None, hs=None) == OK
     assert lib.nvfp4_last_hip_error() == 0
+
+
+def test_binding_checks_caller_buffers_before_any_call():
+    """Buffers the caller passes in (codes, scales, tensor scales, out) are
+    checked for dtype, shape and layout before anything reaches the library:
+    a smaller out or codes buffer would otherwise be written past its end."""
+    import torch
+    u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)  # noqa: E731
+    f32 = lambda *s: torch.zeros(s, dtype=torch.float32)  # noqa: E731
+    x = torch.zeros(4, 32, dtype=torch.bfloat16)
+    for kw, msg in ((dict(codes=u8(4, 8)), "codes"), (dict(codes=u8(3, 16)), "codes"),
+                    (dict(scales=u8(4, 1)), "scales"), (dict(codes=f32(4, 16)), "codes"),
+                    (dict(codes=u8(4, 32)[:, ::2]), "codes"), (dict(global_scale=f32(0)), "global_scale"),
+                    (dict(global_scale=torch.zeros(1, dtype=torch.float64)), "global_scale")):
+        with pytest.raises(ValueError, match=msg):
+            _lib.quantize(x, **kw)
+    with pytest.raises(ValueError, match="multiple of 16"):
+        _lib.quantize(torch.zeros(4, 24, dtype=torch.bfloat16))
+    M, N, K = 8, 48, 64
+    a = (u8(M, K // 2), u8(M, K // 16), f32(1))
+    w = (u8(N, K // 2), u8(N, K // 16), f32(1))
+    for out, msg in ((f32(M - 1, N), "out must be"), (f32(M, N - 1), "out must be"),
+                     (torch.zeros(M, N, dtype=torch.bfloat16), "dtype"), (f32(N, M).t(), "stride")):
+        with pytest.raises(ValueError, match=msg):
+            _lib.gemm(*a, *w, out=out)
+        with pytest.raises(ValueError, match=msg):
+            _lib.gemm_segmented(*a, *w[:2], f32(2), [16, 32], out=out)
+        with pytest.raises(ValueError, match=msg):
+            _lib.gemm_segmented_gates(*a, *w[:2], f32(2), [16, 32], out=out)
+    with pytest.raises(ValueError, match="a_codes"):
+        _lib.gemm(*a, *w, k=2 * K)                       # k disagrees with the codes' width
+    with pytest.raises(ValueError, match="w_scales"):
+        _lib.gemm(*a, w[0], u8(N, 3), w[2])
+    with pytest.raises(ValueError, match="a_gs"):
+        _lib.gemm(a[0], a[1], f32(0), *w)
+    with pytest.raises(ValueError, match="w_gs"):
+        _lib.gemm(*a, w[0], w[1], torch.zeros(1, dtype=torch.float16))
+    with pytest.raises(ValueError, match="out must be"):
+        _lib.quantize_gemm(torch.zeros(M, K, dtype=torch.bfloat16), f32(1), *w, out=f32(M + 1, N))
+    with pytest.raises(ValueError, match="workspace"):
+        _lib.quantize_gemm(torch.zeros(M, K, dtype=torch.bfloat16), f32(1), *w, workspace=f32(16))
+    with pytest.raises(ValueError, match="h_gs"):
+        _lib.gemm_swiglu_quantize(*a, *w, f32(0))
+    # well-formed CPU tensors reach the device check, which refuses them
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        _lib.gemm(*a, *w, out=f32(M, N))

@@ -1,16 +1,19 @@
-"""Full-size workloads, in the launch configuration the bench times, checked on
-samples the oracle can afford: every tensor is generated and quantized at its
-real shape on the GPU; the oracle computes the tensor scale from the whole
-tensor, re-quantizes sampled rows (bit-exact comparison) and computes sampled
-GEMM outputs (tolerance comparison).  Activation scales are calibrated with
-the amax mode and then applied as static scales, as in the bench."""
+"""Full-size workloads, in the launch configuration the bench times: every
+tensor is generated and quantized at its real shape on the GPU; the oracle
+computes the tensor scale from the whole tensor and re-quantizes EVERY row
+(bit-exact comparison of every code and scale byte, in row chunks on host
+threads), and computes GEMM outputs on sampled rows and columns (tolerance
+comparison: the fp64 GEMM of the full 32K-token shapes is out of the
+oracle's reach).  Activation scales are calibrated with the amax mode and
+then applied as static scales, as in the bench."""
 import numpy as np
 import pytest
 import torch
 
 import nvfp4_w4a4_quantized_05_amd as nv
 from oracle import nvfp4_ref as ref
-from tests.gpu_util import assert_codes_equal, assert_gemm_close, host_f32, need_gpu
+from tests.gpu_util import (assert_codes_equal, assert_gemm_close, assert_quantize_matches_oracle_full, host_f32,
+                            need_gpu)
 from workloads import CONFIGS, activations, normal_weights
 
 pytestmark = pytest.mark.gpu
@@ -24,8 +27,10 @@ def _sample(n, count, seed, extra=()):
 
 
 def _quant_checked(t, rows_sel, what, static=False):
-    """GPU-quantize t (amax mode, or calibrate then static), check sampled rows
-    and the tensor scale against the oracle; returns (GPU quantized, oracle g)."""
+    """GPU-quantize t (amax mode, or calibrate then static); check the tensor
+    scale and every code and scale against the oracle (sampled rows once
+    more through assert_codes_equal, whose report names the first mismatch);
+    returns (GPU quantized, oracle g, host values)."""
     if static:
         g = nv.quantize(t)[2].clone()
         q = nv.quantize(t, g, from_amax=False)
@@ -35,6 +40,8 @@ def _quant_checked(t, rows_sel, what, static=False):
     host = host_f32(t)
     g_or = ref.global_scale(host)
     assert float(q[2].item()) == float(g_or), what
+    n = assert_quantize_matches_oracle_full(t, q[0], q[1], g_or, what)
+    print(f"  {what}: all {n} code and scale bytes match the oracle", flush=True)
     oc, os_, _ = ref.quantize(host[rows_sel], g=g_or)
     assert_codes_equal(q[0][rows_sel].cpu().numpy(), q[1][rows_sel].cpu().numpy(), oc, os_, what)
     return q, g_or, host
@@ -88,6 +95,8 @@ def test_layer_32k_full_size():
         wh[q.name] = host_f32(w)
         wg[q.name] = ref.global_scale(wh[q.name])
         assert float(wq[q.name][2].item()) == float(wg[q.name])
+        nb = assert_quantize_matches_oracle_full(w, wq[q.name][0], wq[q.name][1], wg[q.name], f"W {q.name}")
+        print(f"  W {q.name} [{q.n}x{q.k}]: all {nb} code and scale bytes match the oracle", flush=True)
         del w
     # fused in-projection: concatenate, harmonize on the GPU and in the oracle
     fused = ["qkv", "z", "a", "b"]

@@ -20,22 +20,76 @@ def _run(aq, wq, out_dtype=torch.float32, k=None):
     return y
 
 
+def _selection_weight(N, K):
+    """W [N, K] with one code 2 (= 1.0) per row, at column n % K, every block
+    scale 0x38 (= 1.0) and g_w = 1: y[m, n] = deq(A)[m, n % K] exactly, since
+    each output is a single product."""
+    codes = np.zeros((N, K), np.uint8)
+    codes[np.arange(N), np.arange(N) % K] = 2
+    return ref.pack_codes(codes), np.full((N, K // 16), 0x38, np.uint8), np.float32(1)
+
+
+def _all_code_scale_pairs(M, K):
+    """A [M, K] whose blocks run through every E4M3 scale byte 0x00..0x7E
+    (subnormals and 0 included) and hold all 16 E2M1 codes each, rotated per
+    row, so every (code, scale) pair occurs many times."""
+    nb = K // 16
+    codes = (np.arange(K)[None, :] + np.arange(M)[:, None]) % 16
+    scales = (np.arange(M)[:, None] * nb + np.arange(nb)[None, :]) % 127
+    return ref.pack_codes(codes.astype(np.uint8)), scales.astype(np.uint8), np.float32(1)
+
+
+def _assert_selected_exactly(y, aq, N, K, what):
+    """y[m, n] == deq(A)[m, n % K] bit for bit.  A zero output is +0: the
+    accumulator starts at +0, and the sum of +0 and the -0 product of a
+    negative zero code is +0 under round-to-nearest-even."""
+    deq = ref.dequantize(aq[0], aq[1], 1.0)
+    want = (deq[:, np.arange(N) % K] + 0.0).astype(np.float32)          # -0 -> +0
+    got = y.float().cpu().numpy()
+    bad = np.argwhere(got.view(np.uint32) != want.view(np.uint32))
+    assert bad.size == 0, (f"{what}: {len(bad)} outputs differ from the exact dequantized value, first "
+                           f"{bad[:3].tolist()}: got {got[tuple(bad[0])]!r} want {want[tuple(bad[0])]!r}")
+
+
 def test_identity_weight_dequantizes_every_code_and_scale_exactly():
     """W = I (code 2 = 1.0, scale 1.0, g_w = 1) and g_a = 1: every output is a
-    single product, so y = deq(A) bit for bit, over all 16 codes x 127 scales."""
+    single product, so y = deq(A) bit for bit, over all 16 codes x 127 scales.
+    M = 127 and one 256-wide tile: the generic kernel."""
     need_gpu()
     K = 256
     codes = np.tile(np.arange(16, dtype=np.uint8), (127, K // 16))      # [127, K] one code per value
     scales = np.repeat(np.arange(127, dtype=np.uint8)[:, None], K // 16, axis=1)
     ac = ref.pack_codes(codes)
-    wc = ref.pack_codes(np.eye(K, dtype=np.uint8) * 2)
-    ws = np.full((K, K // 16), 0x38, np.uint8)
     for dt in (torch.float32, torch.bfloat16):
-        y = _run((ac, scales, np.float32(1)), (wc, ws, np.float32(1)), out_dtype=dt)
-        want = ref.dequantize(ac, scales, 1.0)
-        got = y.float().cpu().numpy().astype(np.float64)
-        assert np.array_equal(got, want)
-        assert np.array_equal(np.signbit(got[want == 0]), np.zeros_like(got[want == 0], bool)) or True
+        y = _run((ac, scales, np.float32(1)), _selection_weight(K, K), out_dtype=dt)
+        _assert_selected_exactly(y, (ac, scales), K, K, f"generic kernel {dt}")
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_exact_dequant_through_streaming_kernel(dt):
+    """M = N = 4096, K = 256: 256 output tiles of 256 x 256 with K % 128 == 0
+    and aligned operands, the shape class of the large-tile streaming kernel
+    (the bench's prefill GEMMs); every (code, scale) pair, bit for bit."""
+    need_gpu()
+    M = N = 4096
+    K = 256
+    aq = _all_code_scale_pairs(M, K)
+    y = _run(aq, _selection_weight(N, K), out_dtype=dt)
+    _assert_selected_exactly(y, aq, N, K, f"streaming kernel {dt}")
+
+
+@pytest.mark.parametrize("m", [1, 16, 64])
+def test_exact_dequant_through_decode_kernel(m):
+    """M <= 64 with K % 256 == 0: the decode kernel; K = 4096 gives 256
+    blocks per row, so even one row runs through all 127 scales and every
+    block holds all 16 codes; bit for bit, fp32 and bf16 output."""
+    need_gpu()
+    N, K = 4096, 4096
+    aq = _all_code_scale_pairs(m, K)
+    wq = _selection_weight(N, K)
+    for dt in (torch.float32, torch.bfloat16):
+        y = _run(aq, wq, out_dtype=dt)
+        _assert_selected_exactly(y, aq, N, K, f"decode kernel M={m} {dt}")
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])

@@ -57,7 +57,8 @@ def test_harmonize_power_of_two_ratios_exact():
 
 def test_fused_gdn_fused_variants():
     """C4: naive fused, harmonized fused and segmented epilogue against their
-    oracles, and harmonized against per-module, on sampled rows of X."""
+    oracles on every output element (4096 tokens x 12384 columns), and
+    harmonized against per-module."""
     need_gpu()
     cfg = CONFIGS["fused_gdn"]
     kind, rows, cols, dtype = cfg["x"]
@@ -80,21 +81,25 @@ def test_fused_gdn_fused_variants():
         seg = nv.gemm_segmented(ac, as_, ga, gpu_u8(wc), gpu_u8(ws), gs_dev, [q[0].shape[0] for _, q in mods])
         torch.cuda.synchronize()
 
-        rng = np.random.default_rng(0)
-        sel = np.sort(rng.choice(rows, 96, replace=False))
-        a_s = (oa[0][sel], oa[1][sel], oa[2])
+        # every output element of the 4096 x 12384 results against the fp64 oracle
+        a_s = oa
         Yn, Sn = ref.naive_fused_ref(*a_s, wc, ws, gs)
-        assert_gemm_close(naive[sel], Yn, Sn, "naive fused")
+        assert_gemm_close(naive, Yn, Sn, "naive fused")
+        del Yn, Sn
         Ys, Ss = ref.gemm_segmented_ref(*a_s, wc, ws, gs, [q[0].shape[0] for _, q in mods])
-        assert_gemm_close(seg[sel], Ys, Ss, "segmented epilogue")
+        assert_gemm_close(seg, Ys, Ss, "segmented epilogue")
+        del Ys, Ss
         hs, hg, _, _ = ref.harmonize_ref([q[1] for _, q in mods], gs)
+        assert np.array_equal(ws_dev.cpu().numpy(), hs) and float(shared.item()) == float(hg)
         Yh, Sh = ref.gemm_ref(*a_s, wc, hs, hg)
-        assert_gemm_close(harm[sel], Yh, Sh, "harmonized fused")
+        assert_gemm_close(harm, Yh, Sh, "harmonized fused")
+        del Yh, Sh
         # harmonized vs the per-module result: only E4M3 re-rounding separates them
         row = 0
+        harm_h = harm.cpu().numpy().astype(np.float64)
         for name, (c, s, g) in mods:
             Yp, Sp = ref.gemm_ref(*a_s, c, s, g)
-            block = harm[sel][:, row:row + c.shape[0]].cpu().numpy().astype(np.float64)
+            block = harm_h[:, row:row + c.shape[0]]
             rel = np.linalg.norm(block - Yp) / max(np.linalg.norm(Yp), 1e-300)
             print(f"  {name}: harmonized vs per-module relative error {rel:.3e}; "
                   f"naive/per-module scale ratio {float(gs[0]) / float(g):.4f}", flush=True)

@@ -6,15 +6,16 @@ Two checks per shape:
     |v - Y| <= 1e-4 Sabs for gate and up, carried through h = silu(g) u
     (|silu'| <= 1.1, |d h / d u| = |silu(g)|), plus a few fp32 ulp and
     |g| 2^-22 relative (the hardware exp2 of g log2 e);
-  * the codes and scales bit-identical to nvfp4_quantize of that h with the
-    same tensor scale (the quantize kernel itself is pinned to the oracle)."""
+  * the codes and scales bit-identical to the oracle's quantization of that
+    h (every row; h is the kernel's own fp32 output, so both sides quantize
+    the same values) with the same tensor scale, and to nvfp4_quantize of h."""
 import numpy as np
 import pytest
 import torch
 
 import nvfp4_w4a4_quantized_05_amd as nv
 from oracle import nvfp4_ref as ref
-from tests.gpu_util import GEMM_RTOL, assert_codes_equal, host_f32, need_gpu
+from tests.gpu_util import GEMM_RTOL, assert_codes_equal, assert_quantize_matches_oracle_full, host_f32, need_gpu
 from workloads import activations, normal_weights
 
 pytestmark = pytest.mark.gpu
@@ -41,6 +42,9 @@ def test_swiglu_quantize_epilogue(M, F, K, sample):
     assert torch.isnan(h[:, F:]).all(), "h written past column F"
     hv = h[:, :F].contiguous()
     del h
+    assert float(hg.item()) == float(ref.global_scale(host_f32(hv))), "h tensor scale"
+    n = assert_quantize_matches_oracle_full(hv, codes, scales, np.float32(hg.item()), "fused vs oracle quantize of h")
+    print(f"  all {n} code and scale bytes of h match the oracle", flush=True)
     c2, s2, _ = nv.quantize(hv, hg, from_amax=False)
     torch.cuda.synchronize()
     assert_codes_equal(codes, scales, c2.cpu().numpy(), s2.cpu().numpy(), "fused vs nvfp4_quantize of h")

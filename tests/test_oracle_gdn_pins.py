@@ -95,3 +95,35 @@ def test_linear_in_start_state_and_values_and_scale_free_in_q_k():
     o1, S1, _, _ = G.gdn_recurrence_ref(q, k, v, g, beta)
     o2, S2, _, _ = G.gdn_recurrence_ref(q * 7.5, k * 0.02, v, g, beta)
     assert np.allclose(o1, o2, rtol=1e-12, atol=1e-14) and np.allclose(S1, S2, rtol=1e-12, atol=1e-14)
+
+
+def test_split_projection_rows_reads_each_part_from_its_columns():
+    """Projection rows assembled from known parts (q, k, v, g, beta placed at
+    chosen columns with gaps and in a scrambled order, each part holding
+    values no other part holds) come back part by part; v_col = -1 gives
+    v = 0.  A swapped pair of column arguments, a wrong head count or a
+    transposed reshape returns another part's values and fails."""
+    rng = np.random.default_rng(6)
+    T, n_qk, n_v, d = 5, 2, 4, 8
+    parts = {"q": rng.uniform(100, 101, (T, n_qk, d)), "k": rng.uniform(200, 201, (T, n_qk, d)),
+             "v": rng.uniform(300, 301, (T, n_v, d)), "g": rng.uniform(-2, -1, (T, n_v)),
+             "beta": rng.uniform(0.1, 0.9, (T, n_v))}
+    # column order beta | pad | v | g | pad | k | q | pad
+    order = ["beta", None, "v", "g", None, "k", "q", None]
+    cols, blocks, c = {}, [], 0
+    for name in order:
+        blk = np.full((T, 3), -7.0) if name is None else parts[name].reshape(T, -1)
+        if name is not None:
+            cols[name] = c
+        blocks.append(blk)
+        c += blk.shape[1]
+    x = np.concatenate(blocks, axis=1)
+    q, k, v, g, beta = G.split_projection_rows(x, cols["q"], cols["k"], cols["v"], cols["g"], cols["beta"],
+                                               n_qk, n_v, d=d)
+    for name, got in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        assert got.shape == parts[name].shape, name
+        assert np.array_equal(got, parts[name]), name
+    _, _, v0, g0, b0 = G.split_projection_rows(x, cols["q"], cols["k"], -1, cols["g"], cols["beta"], n_qk, n_v,
+                                               d=d)
+    assert v0.shape == (T, n_v, d) and not np.any(v0)
+    assert np.array_equal(g0, parts["g"]) and np.array_equal(b0, parts["beta"])
