@@ -107,3 +107,26 @@ def assert_quantize_matches_oracle_full(x: torch.Tensor, codes: torch.Tensor, sc
     firsts = [r[2] for r in res if r[2]]
     assert n_s == 0 and n_c == 0, f"{what}: {n_s} scale and {n_c} code-byte mismatches; first: {firsts[:1]}"
     return codes.numel() + scales.numel()
+
+
+def oracle_quantize_host(x, g=None, chunk_rows=512):
+    """ref.quantize of a host tensor (numpy or CPU torch, any float dtype),
+    in row chunks on host threads; g = None takes the tensor scale of the
+    whole tensor (ref.global_scale).  Same bytes as ref.quantize(x, g)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    if isinstance(x, torch.Tensor):
+        x = x.detach().float().cpu().numpy()
+    x = np.asarray(x, dtype=np.float32)
+    g = ref.global_scale(x) if g is None else np.float32(g)
+    rows = x.shape[0]
+    with ThreadPoolExecutor(oracle_threads()) as ex:
+        parts = list(ex.map(lambda r0: ref.quantize(x[r0:r0 + chunk_rows], g=g), range(0, rows, chunk_rows)))
+    if not parts:
+        return ref.quantize(x, g=g)
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]), g
+
+
+def to_gpu_quantized(q):
+    """(codes, scales, g) from the host oracle, as device tensors."""
+    return gpu_u8(q[0]), gpu_u8(q[1]), gpu_f32(q[2])

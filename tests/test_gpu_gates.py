@@ -13,7 +13,8 @@ import torch
 
 import nvfp4_w4a4_quantized_05_amd as nv
 from oracle import nvfp4_ref as ref
-from tests.gpu_util import GEMM_RTOL, assert_gemm_close, host_f32, need_gpu
+from tests.gpu_util import (GEMM_RTOL, assert_codes_equal, assert_gemm_close, gpu_u8, host_f32, need_gpu,
+                            oracle_quantize_host)
 from workloads import activations, normal_weights
 
 pytestmark = pytest.mark.gpu
@@ -33,10 +34,14 @@ def _case(M, K, rows, decay, write, seed, rows_sample=None):
     dev = need_gpu()
     x = activations("t3_outlier1pct", M, K, seed=seed, device=dev)
     a = nv.quantize(x)
-    mods = [nv.quantize(normal_weights(r, K, 0.02, seed=seed * 10 + i, device=dev)) for i, r in enumerate(rows)]
-    wc = torch.cat([m[0] for m in mods])
-    wsc = torch.cat([m[1] for m in mods])
-    mgs = torch.cat([m[2] for m in mods])
+    # weights quantized by the oracle on the host (the GPU quantizer is pinned elsewhere)
+    omods = [oracle_quantize_host(normal_weights(r, K, 0.02, seed=seed * 10 + i, device="cpu"))
+             for i, r in enumerate(rows)]
+    ow_c = np.concatenate([m[0] for m in omods])
+    ow_s = np.concatenate([m[1] for m in omods])
+    ow_g = np.array([m[2] for m in omods], dtype=np.float32)
+    wc, wsc = gpu_u8(ow_c), gpu_u8(ow_s)
+    mgs = torch.from_numpy(ow_g).to(dev)
     n_dec = rows[decay] if decay >= 0 else 1
     a_log, dt_bias = gate_params(n_dec, seed)
     gpu = dict(decay_module=decay, a_log=torch.from_numpy(a_log).to(dev) if decay >= 0 else None,
@@ -48,9 +53,14 @@ def _case(M, K, rows, decay, write, seed, rows_sample=None):
             gate_cols[starts[m]:starts[m + 1]] = True
     sample = np.arange(M) if rows_sample is None else rows_sample
     sample_t = torch.from_numpy(sample).to(dev)
-    ah = (a[0][sample_t].cpu().numpy(), a[1][sample_t].cpu().numpy(), np.float32(a[2].item()))
-    G, Y, S = ref.gemm_segmented_gates_ref(*ah, wc.cpu().numpy(), wsc.cpu().numpy(), mgs.cpu().numpy(), rows,
-                                           decay, a_log, dt_bias, write)
+    # activations: the oracle's quantization of the sampled rows with the
+    # oracle's tensor scale of the whole tensor, equal to the GPU's bytes
+    xh = host_f32(x)
+    ah = ref.quantize(xh[sample], g=ref.global_scale(xh))
+    assert float(a[2].item()) == float(ah[2])
+    assert_codes_equal(a[0][sample_t], a[1][sample_t], ah[0], ah[1], "activations")
+    del xh
+    G, Y, S = ref.gemm_segmented_gates_ref(*ah, ow_c, ow_s, ow_g, rows, decay, a_log, dt_bias, write)
     for od in (torch.float32, torch.bfloat16):
         y = nv.gemm_segmented_gates(*a, wc, wsc, mgs, rows, out_dtype=od, **gpu)
         y0 = nv.gemm_segmented(*a, wc, wsc, mgs, rows, out_dtype=od)

@@ -7,7 +7,8 @@ import torch
 
 import nvfp4_w4a4_quantized_05_amd as nv
 from oracle import nvfp4_ref as ref
-from tests.gpu_util import assert_codes_equal, assert_gemm_close, host_f32, need_gpu
+from tests.gpu_util import (assert_codes_equal, assert_gemm_close, host_f32, need_gpu, oracle_quantize_host,
+                            to_gpu_quantized)
 from tests.test_gpu_quantize import bf16_tie_blocks
 from workloads import activations, normal_weights
 
@@ -15,8 +16,10 @@ pytestmark = pytest.mark.gpu
 
 
 def _weights(N, K, seed):
-    w = normal_weights(N, K, 0.02, seed=seed, device="cuda")
-    return nv.quantize(w)
+    """Weights quantized by the oracle on the host, on the device, and the
+    oracle's (codes, scales, g) for the reference GEMM."""
+    oq = oracle_quantize_host(normal_weights(N, K, 0.02, seed=seed, device="cpu"))
+    return to_gpu_quantized(oq), oq
 
 
 def _two_calls(x, g, wq, out_dtype):
@@ -34,7 +37,7 @@ def test_one_kernel_path_is_bit_identical_to_two_calls(M, N, K):
     assert lib.nvfp4_quantize_gemm_workspace_size(M, N, K, 1, 1) == 0
     x = activations("t3_outlier1pct", M, K, seed=M + N, device="cuda")
     g = nv.quantize(x)[2].clone()
-    wq = _weights(N, K, seed=N)
+    wq, _ = _weights(N, K, seed=N)
     for od in (torch.bfloat16, torch.float32):
         y = nv.quantize_gemm(x, g, *wq, out_dtype=od)
         y2 = _two_calls(x, g, wq, od)
@@ -51,7 +54,7 @@ def test_workspace_path_is_bit_identical_to_two_calls(shape):
     assert nv.load().nvfp4_quantize_gemm_workspace_size(M, N, K, 1, 1) > 0
     x = activations("t3_outlier1pct", M, K, seed=M * 7 + K, device="cuda")
     g = nv.quantize(x)[2].clone()
-    wq = _weights(N, K, seed=K)
+    wq, _ = _weights(N, K, seed=K)
     y = nv.quantize_gemm(x, g, *wq, out_dtype=torch.bfloat16)
     y2 = _two_calls(x, g, wq, torch.bfloat16)
     torch.cuda.synchronize()
@@ -67,18 +70,19 @@ def test_row_stride_and_input_dtype_against_the_oracle(dtype):
     M, N, K = 2, 5120, 1024
     xs = activations("t3_outlier1pct", M, 2 * K, seed=11, device="cuda", dtype=dtype)
     x = xs[:, :K]                              # row stride 2K
-    g = nv.quantize(x.contiguous())[2].clone()
-    wq = _weights(N, K, seed=12)
+    xh = host_f32(x.contiguous())
+    g_or = ref.global_scale(xh)                # calibrated static scale, from the oracle
+    g = torch.tensor([g_or], dtype=torch.float32, device="cuda")
+    wq, wh = _weights(N, K, seed=12)
     fused = nv.load().nvfp4_quantize_gemm_workspace_size(M, N, K, 1 if dtype == torch.bfloat16 else 0, 0) == 0
     assert fused == (dtype == torch.bfloat16)
     y = nv.quantize_gemm(x, g, *wq, out_dtype=torch.float32)
     y2 = _two_calls(x.contiguous(), g, wq, torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
-    oa = ref.quantize(host_f32(x.contiguous()), g=np.float32(g.item()))
+    oa = ref.quantize(xh, g=g_or)
     a = nv.quantize(x.contiguous(), g, from_amax=False)
     assert_codes_equal(a[0], a[1], oa[0], oa[1], f"strided X {dtype}")
-    wh = (wq[0].cpu().numpy(), wq[1].cpu().numpy(), np.float32(wq[2].item()))
     Y, S = ref.gemm_ref(*oa, *wh)
     assert_gemm_close(y, Y, S, f"quantize_gemm {dtype} X")
 
@@ -96,7 +100,7 @@ def test_one_kernel_path_on_exact_ties():
     xt = torch.from_numpy(x).to(torch.bfloat16).cuda()
     gt = torch.tensor([g], dtype=torch.float32, device="cuda")
     assert nv.load().nvfp4_quantize_gemm_workspace_size(M, N, K, 1, 0) == 0
-    wq = _weights(N, K, seed=21)
+    wq, wh = _weights(N, K, seed=21)
     y = nv.quantize_gemm(xt, gt, *wq, out_dtype=torch.float32)
     y2 = _two_calls(xt, gt, wq, torch.float32)
     torch.cuda.synchronize()
@@ -104,6 +108,5 @@ def test_one_kernel_path_on_exact_ties():
     oa = ref.quantize(x, g=g)
     a = nv.quantize(xt, gt, from_amax=False)
     assert_codes_equal(a[0], a[1], oa[0], oa[1], "tie rows")
-    wh = (wq[0].cpu().numpy(), wq[1].cpu().numpy(), np.float32(wq[2].item()))
     Y, S = ref.gemm_ref(*oa, *wh)
     assert_gemm_close(y, Y, S, "quantize_gemm tie rows")

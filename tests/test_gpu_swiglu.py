@@ -15,7 +15,8 @@ import torch
 
 import nvfp4_w4a4_quantized_05_amd as nv
 from oracle import nvfp4_ref as ref
-from tests.gpu_util import GEMM_RTOL, assert_codes_equal, assert_quantize_matches_oracle_full, host_f32, need_gpu
+from tests.gpu_util import (GEMM_RTOL, assert_codes_equal, assert_quantize_matches_oracle_full, host_f32, need_gpu,
+                            oracle_quantize_host, to_gpu_quantized)
 from workloads import activations, normal_weights
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +31,12 @@ def test_swiglu_quantize_epilogue(M, F, K, sample):
     print(f"[swiglu] M={M} F={F} K={K}", flush=True)
     x = activations("t3_outlier1pct", M, K, seed=M + F, device=dev)
     a = nv.quantize(x)
-    w = nv.quantize(normal_weights(2 * F, K, 0.015, seed=F, device=dev))
+    xh = host_f32(x)
+    g_a = ref.global_scale(xh)
+    assert float(a[2].item()) == float(g_a)
+    assert_quantize_matches_oracle_full(x, a[0], a[1], g_a, "activations")
+    ow = oracle_quantize_host(normal_weights(2 * F, K, 0.015, seed=F, device="cpu"))   # weights from the oracle
+    w = to_gpu_quantized(ow)
     h = torch.full((M, F + 8), float("nan"), dtype=torch.float32, device=dev)     # ldh > F
     nv.gemm_swiglu_quantize(*a, *w, torch.ones(1, device=dev), h=h)               # h for calibration
     hg = nv.quantize(h[:, :F].contiguous())[2].clone()                            # amax / 2688
@@ -50,9 +56,9 @@ def test_swiglu_quantize_epilogue(M, F, K, sample):
     assert_codes_equal(codes, scales, c2.cpu().numpy(), s2.cpu().numpy(), "fused vs nvfp4_quantize of h")
     rows = np.arange(M) if sample is None else np.array(sample)
     rows_t = torch.from_numpy(rows).to(dev)
-    ah = (a[0][rows_t].cpu().numpy(), a[1][rows_t].cpu().numpy(), np.float32(a[2].item()))
-    wh = (w[0].cpu().numpy(), w[1].cpu().numpy(), np.float32(w[2].item()))
-    H, G, U, SG, SU = ref.gemm_swiglu_ref(*ah, *wh)
+    ah = ref.quantize(xh[rows], g=g_a)            # the oracle's activations (equal to the GPU's, checked above)
+    del xh
+    H, G, U, SG, SU = ref.gemm_swiglu_ref(*ah, *ow)
     eg, eu = GEMM_RTOL * SG, GEMM_RTOL * SU
     # plus the fp32 evaluation: a few ulp, and |g| 2^-23 relative from the exp2 argument's rounding
     tol = 1.1 * (np.abs(U) + eu) * eg + (np.abs(ref.silu(G)) + 1.1 * eg) * eu + \
