@@ -65,7 +65,9 @@ typedef enum {
   NVFP4_ERR_ALIGN = 5,     /* a pointer is not aligned as documented           */
   NVFP4_ERR_WORKSPACE = 6, /* workspace too small                              */
   NVFP4_ERR_HIP = 7,       /* a HIP launch failed; see nvfp4_last_hip_error()  */
-  NVFP4_ERR_ALIAS = 8      /* an output overlaps an input it must not overlap  */
+  NVFP4_ERR_ALIAS = 8,     /* an output overlaps an input it must not overlap  */
+  NVFP4_ERR_TOO_LARGE = 9  /* more than the allocation-free entry point's static
+                              scratch (nvfp4_quantize_gemm_no_alloc)         */
 } nvfp4_status_t;
 
 typedef enum { NVFP4_IN_F32 = 0, NVFP4_IN_BF16 = 1 } nvfp4_in_t;
@@ -319,6 +321,39 @@ NVFP4_API nvfp4_status_t nvfp4_quantize_gemm(const void* x, int32_t in_dtype, in
  * steps, else M*K/2 rounded up to 256 plus M*K/16 (codes, then scales). */
 NVFP4_API size_t nvfp4_quantize_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t in_dtype,
                                                     int32_t out_dtype);
+
+/*
+ * nvfp4_quantize_gemm_no_alloc -- nvfp4_quantize_gemm for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It takes no workspace: where
+ * nvfp4_quantize_gemm would quantize the activations into the caller's
+ * workspace, this call uses a static device array of
+ * nvfp4_quantize_gemm_no_alloc_max_bytes() bytes (4 MiB) that the library
+ * holds on every GPU it runs on until the process ends.  It calls no
+ * hipMalloc, hipFree or allocating library routine; on its first call on a
+ * device it looks up that device's copy of the array (hipGetSymbolAddress).
+ *
+ * Arguments, layouts and results are those of nvfp4_quantize_gemm (same
+ * kernels, same bytes) without workspace and workspace_bytes.  The caller
+ * still owns x, y and the weights.
+ *
+ * Limit: nvfp4_quantize_gemm_workspace_size(M, N, K, in_dtype, out_dtype)
+ * (about M * K * 9/16 bytes) must not exceed the array: 64 rows up to
+ * K = 116,496, 910 rows at K = 8192, 1,456 rows at K = 5120.  Larger
+ * problems return NVFP4_ERR_TOO_LARGE before anything is enqueued.  The array keeps the last call's contents (nothing in it has to
+ * start at zero: every call writes what it reads).  All calls on one GPU
+ * share it, so calls that overlap in time on one GPU (several streams or
+ * host threads without ordering between them) race on it and may give wrong
+ * results; calls ordered on one stream are safe.
+ */
+NVFP4_API nvfp4_status_t nvfp4_quantize_gemm_no_alloc(const void* x, int32_t in_dtype, int64_t ldx,
+                                                      const float* a_gs, const uint8_t* w_codes,
+                                                      const uint8_t* w_scales, const float* w_gs, int64_t M,
+                                                      int64_t N, int64_t K, void* y, int32_t out_dtype,
+                                                      int64_t ldy, void* stream);
+
+/* Bytes of the static scratch of nvfp4_quantize_gemm_no_alloc, per GPU. */
+NVFP4_API size_t nvfp4_quantize_gemm_no_alloc_max_bytes(void);
 
 /*
  * nvfp4_harmonize_fused_scales -- re-express the block scales of modules

@@ -16,4 +16,5 @@ from ._lib import (  # noqa: F401
     load,
     quantize,
     quantize_gemm,
+    quantize_gemm_no_alloc,
 )

@@ -21,10 +21,11 @@ OUT_F32, OUT_BF16 = 0, 1
 SCALE_GIVEN, SCALE_FROM_AMAX = 0, 1
 STATUS_NAMES = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_DTYPE",
                 4: "NVFP4_ERR_MODE", 5: "NVFP4_ERR_ALIGN", 6: "NVFP4_ERR_WORKSPACE",
-                7: "NVFP4_ERR_HIP", 8: "NVFP4_ERR_ALIAS"}
+                7: "NVFP4_ERR_HIP", 8: "NVFP4_ERR_ALIAS", 9: "NVFP4_ERR_TOO_LARGE"}
 EXPORTS = ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_segmented", "nvfp4_gemm_segmented_gates",
            "nvfp4_quantize_gemm", "nvfp4_gdn_recurrence", "nvfp4_gemm_swiglu_quantize",
-           "nvfp4_quantize_gemm_workspace_size", "nvfp4_harmonize_fused_scales",
+           "nvfp4_quantize_gemm_workspace_size", "nvfp4_quantize_gemm_no_alloc",
+           "nvfp4_quantize_gemm_no_alloc_max_bytes", "nvfp4_harmonize_fused_scales",
            "nvfp4_gemm_workspace_size", "nvfp4_status_string", "nvfp4_last_hip_error")
 
 _lib = None
@@ -68,6 +69,10 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_quantize_gemm.restype = i32
     lib.nvfp4_quantize_gemm_workspace_size.argtypes = [i64, i64, i64, i32, i32]
     lib.nvfp4_quantize_gemm_workspace_size.restype = sz
+    lib.nvfp4_quantize_gemm_no_alloc.argtypes = [vp, i32, i64, vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp]
+    lib.nvfp4_quantize_gemm_no_alloc.restype = i32
+    lib.nvfp4_quantize_gemm_no_alloc_max_bytes.argtypes = []
+    lib.nvfp4_quantize_gemm_no_alloc_max_bytes.restype = sz
     lib.nvfp4_harmonize_fused_scales.argtypes = [vp, vp, ctypes.POINTER(i64), i32, i64, vp, vp, vp]
     lib.nvfp4_harmonize_fused_scales.restype = i32
     lib.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64, i32]
@@ -352,6 +357,34 @@ def quantize_gemm(x: torch.Tensor, a_gs: torch.Tensor, w_codes, w_scales, w_gs, 
     st = lib.nvfp4_quantize_gemm(_ptr(x), dt, x.stride(0), _ptr(a_gs), _ptr(w_codes), _ptr(w_scales), _ptr(w_gs),
                                  M, N, K, _ptr(out), od, out.stride(0), ws_ptr, ws_have, _stream(stream))
     _check(st, "nvfp4_quantize_gemm")
+    return out
+
+
+def quantize_gemm_no_alloc(x: torch.Tensor, a_gs: torch.Tensor, w_codes, w_scales, w_gs, *,
+                           out_dtype=torch.float32, out: torch.Tensor | None = None, stream=None):
+    """quantize_gemm without a workspace: the library's static device scratch
+    holds the quantized activations (nvfp4_quantize_gemm_no_alloc; calls
+    that overlap on one GPU race on it).  Allocates out only if not given."""
+    if x.dim() != 2 or x.stride(1) != 1 or x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be a 2-D bf16 or fp32 tensor with unit column stride")
+    M, K = x.shape
+    N = w_codes.shape[0]
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    _u8_matrix(w_codes, (N, K // 2), "w_codes")
+    _u8_matrix(w_scales, (N, K // 16), "w_scales")
+    _f32_scalars(a_gs, 1, "a_gs")
+    _f32_scalars(w_gs, 1, "w_gs")
+    dt = IN_BF16 if x.dtype == torch.bfloat16 else IN_F32
+    od = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[out_dtype]
+    if out is not None:
+        _out_matrix(out, M, N, out_dtype)
+    _need_gpu(x, a_gs, w_codes, w_scales, w_gs, out)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    st = load().nvfp4_quantize_gemm_no_alloc(_ptr(x), dt, x.stride(0), _ptr(a_gs), _ptr(w_codes), _ptr(w_scales),
+                                             _ptr(w_gs), M, N, K, _ptr(out), od, out.stride(0), _stream(stream))
+    _check(st, "nvfp4_quantize_gemm_no_alloc")
     return out
 
 

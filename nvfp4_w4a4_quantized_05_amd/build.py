@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnvfp4.so")
-SOURCES = ["nvfp4_quantize.hip", "nvfp4_gemm.hip", "nvfp4_harmonize.hip", "nvfp4_gdn.hip", "nvfp4_api.cpp"]
+SOURCES = ["nvfp4_quantize.hip", "nvfp4_gemm.hip", "nvfp4_harmonize.hip", "nvfp4_gdn.hip", "nvfp4_noalloc.hip",
+           "nvfp4_api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 ops are disabled on purpose: the compiler must not form

@@ -41,6 +41,54 @@ nvfp4_status_t gemm_checked(const uint8_t* a_codes, const uint8_t* a_scales, con
                                        out_dtype == NVFP4_OUT_BF16, ldy, (hipStream_t)stream));
 }
 
+
+// Argument checks of nvfp4_quantize_gemm and its allocation-free variant
+// (everything but the workspace), before any HIP call.
+nvfp4_status_t quantize_gemm_checks(const void* x, int32_t in_dtype, int64_t ldx, const float* a_gs,
+                                    const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int64_t M,
+                                    int64_t N, int64_t K, void* y, int32_t out_dtype, int64_t ldy) {
+  if (in_dtype != NVFP4_IN_F32 && in_dtype != NVFP4_IN_BF16) return NVFP4_ERR_DTYPE;
+  if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_DTYPE;
+  if (M < 0 || N <= 0 || K <= 0 || K % 16 != 0 || ldx < K || ldy < N) return NVFP4_ERR_SHAPE;
+  if (M > INT_MAX || N > INT_MAX || K > INT_MAX || M > INT64_MAX / ldx / 4) return NVFP4_ERR_SHAPE;
+  if (M == 0) return NVFP4_OK;
+  if (!x || !a_gs || !w_codes || !w_scales || !w_gs || !y) return NVFP4_ERR_NULL;
+  const int64_t esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
+  if (!aligned(x, 16) || (ldx * esize) % 16 != 0 || !aligned(a_gs, 4) || !aligned(w_gs, 4) ||
+      !aligned(y, out_dtype == NVFP4_OUT_BF16 ? 2 : 4))
+    return NVFP4_ERR_ALIGN;
+  if ((M * (K / 16) + 255) / 256 > (int64_t)INT_MAX) return NVFP4_ERR_SHAPE;
+  if (((M + 127) / 128) * ((N + 127) / 128) > (int64_t)INT_MAX) return NVFP4_ERR_SHAPE;
+  if (nvfp4_quantize_gemm_workspace_size(M, N, K, in_dtype, out_dtype) == 0 &&
+      (!aligned(w_codes, 16) || !aligned(w_scales, 8)))
+    return NVFP4_ERR_ALIGN;  // the one-kernel form reads W with 16- and 4-byte loads
+  return NVFP4_OK;
+}
+
+// The launches of a checked quantize + GEMM: one kernel when `need` is 0,
+// else the quantize kernel into ws (codes, then scales 256-byte aligned)
+// and the GEMM from there.
+nvfp4_status_t quantize_gemm_launch(const void* x, int32_t in_dtype, int64_t ldx, const float* a_gs,
+                                    const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs, int64_t M,
+                                    int64_t N, int64_t K, void* y, int32_t out_dtype, int64_t ldy, uint8_t* ws,
+                                    size_t need, void* stream) {
+  nvfp4::ColScales cs{};
+  cs.gs = w_gs;
+  cs.n = 1;
+  cs.end[0] = (int)N;
+  const bool in_bf16 = in_dtype == NVFP4_IN_BF16, out_bf16 = out_dtype == NVFP4_OUT_BF16;
+  if (need == 0)  // one kernel: the decode GEMM quantizes the activations itself
+    return hip_status(nvfp4::launch_quantize_gemm_fused(x, in_bf16, ldx, a_gs, w_codes, w_scales, cs, M, N, K, y,
+                                                        out_bf16, ldy, (hipStream_t)stream));
+  uint8_t* codes = ws;
+  uint8_t* scales = codes + (M * (K / 2) + 255) / 256 * 256;
+  const nvfp4_status_t st = hip_status(nvfp4::launch_quantize(x, in_bf16, M, K, ldx, codes, scales,
+                                                              const_cast<float*>(a_gs), false, (hipStream_t)stream));
+  if (st != NVFP4_OK) return st;
+  return hip_status(nvfp4::launch_gemm(codes, scales, a_gs, w_codes, w_scales, cs, M, N, K, y, out_bf16, ldy,
+                                       (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -227,46 +275,43 @@ nvfp4_status_t nvfp4_quantize_gemm(const void* x, int32_t in_dtype, int64_t ldx,
                                    int64_t M, int64_t N, int64_t K, void* y, int32_t out_dtype, int64_t ldy,
                                    void* workspace, size_t workspace_bytes, void* stream) {
   try {
-    if (in_dtype != NVFP4_IN_F32 && in_dtype != NVFP4_IN_BF16) return NVFP4_ERR_DTYPE;
-    if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_DTYPE;
-    if (M < 0 || N <= 0 || K <= 0 || K % 16 != 0 || ldx < K || ldy < N) return NVFP4_ERR_SHAPE;
-    if (M > INT_MAX || N > INT_MAX || K > INT_MAX || M > INT64_MAX / ldx / 4) return NVFP4_ERR_SHAPE;
-    if (M == 0) return NVFP4_OK;
-    if (!x || !a_gs || !w_codes || !w_scales || !w_gs || !y) return NVFP4_ERR_NULL;
-    const int64_t esize = in_dtype == NVFP4_IN_BF16 ? 2 : 4;
-    if (!aligned(x, 16) || (ldx * esize) % 16 != 0 || !aligned(a_gs, 4) || !aligned(w_gs, 4) ||
-        !aligned(y, out_dtype == NVFP4_OUT_BF16 ? 2 : 4))
-      return NVFP4_ERR_ALIGN;
+    const nvfp4_status_t st = quantize_gemm_checks(x, in_dtype, ldx, a_gs, w_codes, w_scales, w_gs, M, N, K, y,
+                                                   out_dtype, ldy);
+    if (st != NVFP4_OK || M == 0) return st;
     const size_t need = nvfp4_quantize_gemm_workspace_size(M, N, K, in_dtype, out_dtype);
     if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
     if (need > 0 && !workspace) return NVFP4_ERR_NULL;
-    if ((M * (K / 16) + 255) / 256 > (int64_t)INT_MAX) return NVFP4_ERR_SHAPE;
-    nvfp4::ColScales cs{};
-    cs.gs = w_gs;
-    cs.n = 1;
-    cs.end[0] = (int)N;
-    const bool in_bf16 = in_dtype == NVFP4_IN_BF16, out_bf16 = out_dtype == NVFP4_OUT_BF16;
-    if (need == 0) {  // one kernel: the decode GEMM quantizes the activations itself
-      if (!aligned(w_codes, 16) || !aligned(w_scales, 8)) return NVFP4_ERR_ALIGN;
-      return hip_status(nvfp4::launch_quantize_gemm_fused(x, in_bf16, ldx, a_gs, w_codes, w_scales, cs, M, N, K,
-                                                          y, out_bf16, ldy, (hipStream_t)stream));
-    }
-    // two kernels through the workspace: quantize (given scale), then GEMM
-    if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
-    uint8_t* codes = static_cast<uint8_t*>(workspace);
-    uint8_t* scales = codes + (M * (K / 2) + 255) / 256 * 256;
-    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    if (tiles > (int64_t)INT_MAX) return NVFP4_ERR_SHAPE;
-    const nvfp4_status_t st = hip_status(nvfp4::launch_quantize(x, in_bf16, M, K, ldx, codes, scales,
-                                                                const_cast<float*>(a_gs), false,
-                                                                (hipStream_t)stream));
-    if (st != NVFP4_OK) return st;
-    return hip_status(nvfp4::launch_gemm(codes, scales, a_gs, w_codes, w_scales, cs, M, N, K, y, out_bf16, ldy,
-                                         (hipStream_t)stream));
+    if (need > 0 && !aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
+    return quantize_gemm_launch(x, in_dtype, ldx, a_gs, w_codes, w_scales, w_gs, M, N, K, y, out_dtype, ldy,
+                                static_cast<uint8_t*>(workspace), need, stream);
   } catch (...) {
     return NVFP4_ERR_HIP;
   }
 }
+
+nvfp4_status_t nvfp4_quantize_gemm_no_alloc(const void* x, int32_t in_dtype, int64_t ldx, const float* a_gs,
+                                            const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
+                                            int64_t M, int64_t N, int64_t K, void* y, int32_t out_dtype,
+                                            int64_t ldy, void* stream) {
+  try {
+    const nvfp4_status_t st = quantize_gemm_checks(x, in_dtype, ldx, a_gs, w_codes, w_scales, w_gs, M, N, K, y,
+                                                   out_dtype, ldy);
+    if (st != NVFP4_OK || M == 0) return st;
+    const size_t need = nvfp4_quantize_gemm_workspace_size(M, N, K, in_dtype, out_dtype);
+    if (need > nvfp4::kNoAllocScratchBytes) return NVFP4_ERR_TOO_LARGE;
+    void* scratch = nullptr;
+    if (need > 0) {
+      const hipError_t e = nvfp4::no_alloc_scratch(&scratch);
+      if (e != hipSuccess) return hip_status(e);
+    }
+    return quantize_gemm_launch(x, in_dtype, ldx, a_gs, w_codes, w_scales, w_gs, M, N, K, y, out_dtype, ldy,
+                                static_cast<uint8_t*>(scratch), need, stream);
+  } catch (...) {
+    return NVFP4_ERR_HIP;
+  }
+}
+
+size_t nvfp4_quantize_gemm_no_alloc_max_bytes(void) { return nvfp4::kNoAllocScratchBytes; }
 
 nvfp4_status_t nvfp4_harmonize_fused_scales(uint8_t* scales, const float* module_gs,
                                             const int64_t* module_rows, int32_t n_modules,
@@ -306,6 +351,9 @@ const char* nvfp4_status_string(int32_t status) {
     case NVFP4_ERR_WORKSPACE: return "workspace too small";
     case NVFP4_ERR_HIP: return "HIP launch failed";
     case NVFP4_ERR_ALIAS: return "output overlaps an input that is still being read";
+    case NVFP4_ERR_TOO_LARGE:
+      return "the quantized activations need more than the static scratch of nvfp4_quantize_gemm_no_alloc "
+             "(nvfp4_quantize_gemm_no_alloc_max_bytes())";
     default: return "unknown status";
   }
 }

@@ -62,6 +62,14 @@ hipError_t launch_quantize_gemm_fused(const void* x, bool in_bf16, int64_t ldx, 
                                       int64_t M, int64_t N, int64_t K, void* y, bool out_bf16, int64_t ldy,
                                       hipStream_t stream);
 
+// The allocation-free quantize + GEMM keeps the quantized activations in a
+// static device array of this many bytes per GPU (nvfp4_noalloc.hip).
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+
+// Device address of that array on the current device, looked up with
+// hipGetSymbolAddress on the first call per device and kept.
+hipError_t no_alloc_scratch(void** ptr);
+
 hipError_t launch_harmonize(uint8_t* scales, const float* module_gs, const int64_t* module_rows,
                             int32_t n_modules, int64_t K, float* shared_gs, uint32_t* counters,
                             hipStream_t stream);

@@ -11,7 +11,7 @@ from nvfp4_w4a4_quantized_05_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4.h")
 
-OK, NULL, SHAPE, DTYPE, MODE, ALIGN, WORKSPACE, HIP, ALIAS = range(9)
+OK, NULL, SHAPE, DTYPE, MODE, ALIGN, WORKSPACE, HIP, ALIAS, TOO_LARGE = range(10)
 
 # Fake, never-dereferenced device addresses: every call below must fail
 # validation before it would launch anything.
@@ -44,8 +44,8 @@ def test_header_status_codes_match_binding():
 
 
 def test_status_strings(lib):
-    for s in range(9):
-        assert lib.nvfp4_status_string(s)
+    for s in range(10):
+        assert lib.nvfp4_status_string(s) != b"unknown status"
     assert lib.nvfp4_status_string(99) == b"unknown status"
     assert lib.nvfp4_last_hip_error() == 0
 
@@ -304,3 +304,26 @@ def test_binding_checks_caller_buffers_before_any_call():
     # well-formed CPU tensors reach the device check, which refuses them
     with pytest.raises(ValueError, match="GPU tensors only"):
         _lib.gemm(*a, *w, out=f32(M, N))
+
+
+def qgn(lib, x=P16, dt=1, ldx=256, a_gs=P16, M=2, N=64, K=256, y=P16, od=1, ldy=64):
+    return lib.nvfp4_quantize_gemm_no_alloc(x, dt, ldx, a_gs, P16, P16, P16, M, N, K, y, od, ldy, None)
+
+
+def test_quantize_gemm_no_alloc_checks_arguments_and_its_scratch_limit(lib):
+    """Same argument checks as nvfp4_quantize_gemm; a problem whose quantized
+    activations exceed the static scratch is refused before any HIP call."""
+    limit = lib.nvfp4_quantize_gemm_no_alloc_max_bytes()
+    assert limit == 4 << 20
+    assert qgn(lib, M=0) == OK
+    assert qgn(lib, dt=5) == DTYPE and qgn(lib, od=7) == DTYPE
+    assert qgn(lib, K=250, ldx=250) == SHAPE and qgn(lib, ldy=10) == SHAPE and qgn(lib, ldx=100) == SHAPE
+    assert qgn(lib, x=None) == NULL and qgn(lib, y=None) == NULL and qgn(lib, a_gs=None) == NULL
+    assert qgn(lib, x=P_ODD) == ALIGN
+    # need = M*K/2 (rounded up to 256) + M*K/16 against the 4 MiB array
+    assert lib.nvfp4_quantize_gemm_workspace_size(910, 64, 8192, 1, 1) <= limit
+    assert lib.nvfp4_quantize_gemm_workspace_size(911, 64, 8192, 1, 1) > limit
+    assert qgn(lib, M=911, K=8192, ldx=8192) == TOO_LARGE
+    assert qgn(lib, M=64, K=116512, ldx=116512) == TOO_LARGE
+    assert qgn(lib, M=4096, N=4096, K=4096, ldx=4096, ldy=4096) == TOO_LARGE
+    assert b"static scratch" in lib.nvfp4_status_string(TOO_LARGE)
