@@ -10,35 +10,34 @@
 //
 // Exact rounding at fp32 cost.  The quotients are formed approximately in
 // fp32 (a reciprocal and a multiply, a few ulp of error) and rounded by the
-// hardware converters (fp8 for the scale, fp4 for the codes).  That gives
-// the exact-real answer unless the quotient lies within a few ulp of a
-// rounding midpoint, where the decision is taken exactly: with the midpoint
-// t (exact in fp32), fma(t * scale, g, -|x|) is the exact difference
+// hardware converters (fp8 for the scale, fp4 for the codes).  Where the
+// approximate quotient could round differently from the exact one, the
+// decision is taken exactly: with a value t exact in fp32 (a midpoint, or a
+// grid value), fma(t * scale, g, -|x|) is the exact difference
 // t*scale*g - |x| rounded once, so its sign, and whether it is zero (a tie),
 // are exact.
 //
 //  * Block scale: both neighbouring midpoints of the converter's result are
-//    checked that way, always (a few ops per block, no branch).
-//  * Codes: every midpoint of the E2M1 grid has at most 2 mantissa bits, so
-//    "near a midpoint" is read off the low mantissa bits of the approximate
-//    quotient (grid points and zeros pass the test too, harmlessly).  When
-//    any value of the wave's blocks is near, each flagged quotient y is
-//    replaced by the nearby 2-mantissa-bit value m moved by 2^-8 of itself
-//    toward the side the exact test gives (on a tie, toward the even code),
-//    and the converter rounds that.  The move is far smaller than the gap
-//    from m to any other decision point, so flagged grid values keep their
-//    codes.  Generic fp32 data is near for about one value in 10^5; bf16
-//    data far more often (its block maxima share short mantissas with the
-//    tensor maximum, so quotients land on grid points and midpoints), which
-//    is why both paths stay in vector registers, without per-value branches.
+//    checked that way (a few ops per block, no branch).
+//  * Codes: every E2M1 decision point (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5)
+//    has at most 2 mantissa bits, so between two consecutive values with at
+//    most 2 mantissa bits, m1 < m2, the code is constant.  The exact
+//    quotient q lies in [m1, m2] for the pair around it, and the approximate
+//    quotient y rounded to 2 mantissa bits, m, is m1 or m2 (y is off by a few
+//    ulp, far less than half the gap).  The exact sign of m*scale*g - |x|
+//    says on which side of m the exact quotient lies (a zero: on m itself,
+//    a tie if m is a decision point); m moved by 2^-8 of itself to that side
+//    (on a tie, toward the even code) lies strictly inside q's interval, so
+//    the converter's rounding of it is the exact-real code.  This holds for
+//    every value, so every quotient takes the same few ops, with no test or
+//    branch (grid values and values far from a decision point come out
+//    unchanged in code).
 #pragma once
 
 #include "nvfp4_device.h"
 
 namespace nvfp4 {
 namespace {
-
-constexpr uint32_t kNearUlps = 16;  // margin (in ulps) of the near-midpoint test
 
 // Exact E4M3 rounding of bm / (6 g) from the converter's result s0 for an
 // approximate quotient: s0 - 1 if bm lies below the midpoint under s0 (or on
@@ -57,23 +56,22 @@ __device__ __forceinline__ uint32_t exact_scale(uint32_t s0, float v0, float bm,
   return s;
 }
 
-// Near-midpoint key of a quotient's bit pattern b: <= 2 * kNearUlps when b
-// is within kNearUlps ulps of a value with at most 2 mantissa bits.
-__device__ __forceinline__ uint32_t e2m1_near_key(uint32_t b) { return (b + kNearUlps) & 0x1FFFFFu; }
-
-// Settled quotient for a value x whose approximate quotient y lies next to a
-// value with <= 2 mantissa bits, m.  With unit val(s) g: beyond m
+// Settled quotient for a value x with approximate quotient y: m = y rounded
+// to 2 mantissa bits (ties away from zero); with unit val(s) g: beyond m
 // (|x| > |m| val(s) g) the result is |m| moved away from zero, short of it
 // toward zero, and on a tie toward the even code: of the E2M1 decision
 // points 0.25 | 0.75 | 1.25 | 1.75 | 2.5 | 3.5 | 5, exactly those with the
-// first mantissa bit set (0.75, 1.75, 3.5) have an odd code below them.  The
-// sign is y's (also for y = -0).
+// first mantissa bit set (0.75, 1.75, 3.5) have an odd code below them.  So
+// with d = the exact difference m val(s) g - |x| (never -0: the product is
+// >= 0) and b = that mantissa bit of m, "round down" is d > 0, or d = +0
+// and b = 0, i.e. (int)bits(d) >= b.  The sign is y's (also for y = -0).
+// m = 0 stays 0.
 __device__ __forceinline__ float settle_e2m1(float y, float ax, float sval, float g) {
   const uint32_t mb = (__float_as_uint(y) + 0x100000u) & 0x7FE00000u;  // |m|
   const float m = __uint_as_float(mb);
-  const uint32_t even_down = ((mb >> 22) & 1u) ^ 1u;
-  const int d = (int)(__float_as_uint(fmaf(m * sval, g, -ax)) | even_down);  // > 0: round down
-  const float r = fmaf(m, d > 0 ? -0x1p-8f : 0x1p-8f, m);
+  const int b = (int)((mb >> 22) & 1u);
+  const bool down = (int)__float_as_uint(fmaf(m * sval, g, -ax)) >= b;
+  const float r = fmaf(m, down ? -0x1p-8f : 0x1p-8f, m);
   return __uint_as_float((__float_as_uint(r) & 0x7FFFFFFFu) | (__float_as_uint(y) & 0x80000000u));
 }
 
@@ -95,19 +93,8 @@ __device__ __forceinline__ uint32_t quantize_block(const float v[16], float g, f
   const float rcp = s ? __builtin_amdgcn_rcpf(sval * g) : 0.0f;  // zero scale: all magnitudes 0
 
   float y[16];
-  uint32_t key = 0xFFFFFFFFu;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    y[i] = v[i] * rcp;
-    key = min(key, e2m1_near_key(__float_as_uint(y[i])));
-  }
-  if (key <= 2 * kNearUlps) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float ys = settle_e2m1(y[i], fabsf(v[i]), sval, g);
-      y[i] = e2m1_near_key(__float_as_uint(y[i])) <= 2 * kNearUlps ? ys : y[i];
-    }
-  }
+  for (int i = 0; i < 16; ++i) y[i] = settle_e2m1(v[i] * rcp, fabsf(v[i]), sval, g);
   w0 = 0;
   w1 = 0;
   w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[0], y[1], 1.0f, 0);
