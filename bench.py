@@ -337,24 +337,41 @@ def main():
         roofline_q["torch_copy_1gib_gbps"] = round(copy_gbps, 1)
         roofline_q["ratio_to_torch_copy"] = round(q_ach / copy_gbps, 4)
 
-    # amax mode (dynamic activation scale) costs one more read of X
-    amax_ms = None
+    # amax mode (dynamic activation scale): the extra pass over each input
+    # (FROM_AMAX = clear + amax + quantize + finalize) against the quantize
+    # pass with the static scale (GIVEN); amax pass = their difference
+    amax_per_input = {}
     try:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g_tmp = torch.empty(1, dtype=torch.float32, device=dev)
-        e0.record(stream)
-        for _ in range(5):
-            nv.quantize(xs[3], g_tmp, from_amax=True, codes=qbuf[3][0], scales=qbuf[3][1])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        amax_ms = e0.elapsed_time(e1) / 5
-    except Exception:  # noqa: BLE001  (report, never fail the bench on this extra)
-        amax_ms = None
+        for gi, g in enumerate(gemms):
+            xi = g[1]
+            times = {}
+            for label, fa in (("given_ms", False), ("from_amax_ms", True)):
+                vals = []
+                for _ in range(5):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    nv.quantize(xs[xi], g_tmp if fa else calib[xi], from_amax=fa, codes=qbuf[xi][0],
+                                scales=qbuf[xi][1])
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    vals.append(e0.elapsed_time(e1))
+                times[label] = float(np.median(vals))
+            rd = T * xs[xi].shape[1] * 2.0
+            amax_per_input[g[0]] = {
+                "shape": [T, int(xs[xi].shape[1])], "quantize_given_ms": round(times["given_ms"], 4),
+                "quantize_from_amax_ms": round(times["from_amax_ms"], 4),
+                "amax_pass_ms": round(times["from_amax_ms"] - times["given_ms"], 4),
+                "amax_pass_gbps": round(rd / max(times["from_amax_ms"] - times["given_ms"], 1e-6) / 1e6, 1),
+                "sum_gbps": round((qbytes[g[0]] + rd) / (times["from_amax_ms"] * 1e-3) / 1e9, 1)}
+    except Exception as exc:  # noqa: BLE001  (report, never fail the bench on this extra)
+        amax_per_input = {"error": repr(exc)}
 
     extra = {} if args.no_extras else extra_measurements(nv, torch, np, dev, stream, xs, calib, qbuf, ys, in_codes,
                                                          in_scales, in_gs, in_scales_modules, module_gs,
                                                          [P[n].n for n in fused], T)
     if not args.no_extras:
+        extra["configs"] = config_measurements(nv, torch, np, dev, stream)
         extra["gate_error_compression"] = gate_error_compression(nv, torch, np, dev, xs[0], calib[0], wq, w_gates,
                                                                  seed)
         extra["mlp_swiglu_quantize_epilogue"] = mlp_fused(nv, torch, np, dev, stream, xs, calib, qbuf, wq, gemms,
@@ -381,7 +398,7 @@ def main():
         "gemm_ms_per_step": round(gemm_ms_total, 4),
         "quantize_ms_per_step": round(q_ms_total, 4),
         "quantize_gbps": round(sum(qbytes.values()) / (q_ms_total * 1e-3) / 1e9, 1),
-        "quantize_amax_mode_ms_X_d": round(amax_ms, 4) if amax_ms else None,
+        "quantize_amax_per_input": amax_per_input,
         "per_projection": per,
         "harmonize_counters": [int(v) for v in harm_counters.cpu().tolist()],
         "roofline": roofline,
@@ -405,6 +422,173 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows, xs, gemms, wq, fused, P, seed)
     print(json.dumps(out), flush=True)
+
+
+def _pcts(np, vals):
+    return [round(float(np.percentile(vals, q)), 4) for q in (10, 50, 90)]
+
+
+def _timed(torch, np, stream, fn, reps, per_batch=1):
+    """Times of `reps` batches of `per_batch` queued calls of fn(r) (ms per
+    call), from HIP events on the stream the calls run on.  Batches of
+    several calls have the launch queue pre-filled (GPU time, not launch
+    rate)."""
+    for r in range(3):
+        fn(r)
+    torch.cuda.synchronize()
+    out = []
+    for b in range(reps):
+        if per_batch > 1:
+            torch.cuda._sleep(20_000_000)   # keeps the GPU busy while the host enqueues
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(per_batch):
+            fn(b * per_batch + r)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / per_batch)
+    return out
+
+
+def config_measurements(nv, torch, np, dev, stream):
+    """The other workloads, each on its own seeded inputs (besides the
+    32K-token layer that `value` measures): time per call as p10/p50/p90 and
+    the roofline fraction of its bound.
+      tiny        X[16x256] fp32, W[256x256]: amax-mode quantize + GEMM, us
+                  (launch-bound)
+      decode      M in {1, 8, 32, 64} x N = 12288 x K = 5120: GEMM against 8
+                  rotated weight copies (past the 256 MB last-level cache),
+                  and quantize + GEMM; HBM-bound on the weight stream
+      prefill_mlp gate/up 32768x34816x5120 and down 32768x5120x17408 on
+                  Student-t inputs, with their quantize passes
+      fused_gdn   4096 tokens x (8192 + 4096 + 48 + 48) x 5120: harmonize,
+                  naive fused, harmonized fused, segmented and per-module"""
+    from workloads import CONFIGS, activations, normal_weights
+
+    res = {}
+    # tiny: launch-bound
+    cfg = CONFIGS["tiny"]
+    kind, rows, cols, dtype = cfg["x"]
+    x = activations(kind, rows, cols, seed=cfg["seed"], device=dev, dtype=dtype)
+    p = cfg["projections"][0]
+    wq = nv.quantize(normal_weights(p.n, p.k, p.std, seed=cfg["seed"] * 100, device=dev))
+    y = torch.empty((rows, p.n), dtype=torch.float32, device=dev)
+    gx = torch.empty(1, dtype=torch.float32, device=dev)
+    qa = (torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+          torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev))
+
+    def tiny(_r):
+        nv.quantize(x, gx, from_amax=True, codes=qa[0], scales=qa[1])
+        nv.gemm(qa[0], qa[1], gx, *wq, out=y)
+
+    t = _timed(torch, np, stream, tiny, 10, per_batch=100)
+    res["tiny"] = {"shape": "X[16x256] fp32 (amax mode) x W[256x256]", "quantize_plus_gemm_us_p10_p50_p90":
+                   [round(v * 1e3, 2) for v in _pcts(np, t)], "bound": "launch (4 kernels per call)"}
+
+    # decode at N = 12288 (weight stream from HBM)
+    cfg = CONFIGS["decode"]
+    p = cfg["projections"][0]
+    w = nv.quantize(normal_weights(p.n, p.k, p.std, seed=cfg["seed"] * 100, device=dev))
+    copies = [(w[0].clone(), w[1].clone()) for _ in range(8)]
+    wbytes = p.n * p.k * 0.5625
+    dec = {}
+    for m in cfg["ms"]:
+        xm = activations(cfg["x"][0], m, p.k, seed=cfg["seed"], device=dev)
+        g = nv.quantize(xm)[2].clone()
+        a = nv.quantize(xm, g, from_amax=False)
+        ym = torch.empty((m, p.n), dtype=torch.bfloat16, device=dev)
+
+        def gemm_only(r, a=a, ym=ym):
+            nv.gemm(*a, copies[r % 8][0], copies[r % 8][1], w[2], out_dtype=torch.bfloat16, out=ym)
+
+        def chain(r, xm=xm, g=g, a=a, ym=ym):
+            nv.quantize(xm, g, from_amax=False, codes=a[0], scales=a[1])
+            gemm_only(r)
+
+        tg = _timed(torch, np, stream, gemm_only, 10, per_batch=50)
+        tc = _timed(torch, np, stream, chain, 10, per_batch=50)
+        med = float(np.median(tg))
+        dec[str(m)] = {"gemm_us_p10_p50_p90": [round(v * 1e3, 2) for v in _pcts(np, tg)],
+                       "quantize_plus_gemm_us_p10_p50_p90": [round(v * 1e3, 2) for v in _pcts(np, tc)],
+                       "weight_gbps": round(wbytes / (med * 1e-3) / 1e9, 1),
+                       "hbm_frac": round(wbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    res["decode"] = {"shape": f"M x {p.n} x {p.k}, bf16 out, weights rotated over 8 copies",
+                     "bound": "hbm (weights: N K 0.5625 B)", "per_m": dec}
+    del copies, w
+
+    # prefill MLP on Student-t inputs
+    cfg = CONFIGS["prefill_mlp"]
+    T = cfg["rows"]
+    mlp = {}
+    for i, p in enumerate(cfg["projections"]):
+        xk = activations(cfg["x"][0], T, p.k, seed=cfg["seed"] * 10 + i, device=dev)
+        g = nv.quantize(xk)[2].clone()
+        a = nv.quantize(xk, g, from_amax=False)
+        wq = nv.quantize(normal_weights(p.n, p.k, p.std, seed=cfg["seed"] * 100 + i, device=dev))
+        yk = torch.empty((T, p.n), dtype=torch.bfloat16, device=dev)
+        tq = _timed(torch, np, stream, lambda r, xk=xk, g=g, a=a: nv.quantize(xk, g, from_amax=False, codes=a[0],
+                                                                              scales=a[1]), 10)
+        tg = _timed(torch, np, stream, lambda r, a=a, wq=wq, yk=yk: nv.gemm(*a, *wq, out_dtype=torch.bfloat16,
+                                                                            out=yk), 10)
+        fl = 2.0 * T * p.n * p.k
+        qb = T * p.k * QUANT_BYTES_PER_ELEM_BF16
+        mlp[p.name] = {"shape": [T, p.n, p.k], "gemm_ms_p10_p50_p90": _pcts(np, tg),
+                       "gemm_tflops": round(fl / (float(np.median(tg)) * 1e-3) / 1e12, 1),
+                       "gemm_frac_of_peak": round(fl / (float(np.median(tg)) * 1e-3) / 1e12 / PEAK_FP16_MFMA_TFLOPS, 4),
+                       "quantize_ms_p10_p50_p90": _pcts(np, tq),
+                       "quantize_gbps": round(qb / (float(np.median(tq)) * 1e-3) / 1e9, 1),
+                       "quantize_hbm_frac": round(qb / (float(np.median(tq)) * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        del xk, a, wq, yk
+    res["prefill_mlp"] = {"inputs": "Student-t(3), 1% of channels x60", "per_gemm": mlp}
+    torch.cuda.empty_cache()
+
+    # fused GDN in-projection at 4096 tokens
+    cfg = CONFIGS["fused_gdn"]
+    T4 = cfg["rows"]
+    x4 = activations(cfg["x"][0], T4, cfg["x"][2], seed=cfg["seed"], device=dev)
+    a4 = nv.quantize(x4)
+    mods = [nv.quantize(normal_weights(q.n, q.k, q.std, seed=cfg["seed"] * 100 + i, device=dev))
+            for i, q in enumerate(cfg["projections"])]
+    rows4 = [q.n for q in cfg["projections"]]
+    wc = torch.cat([m[0] for m in mods])
+    ws0 = torch.cat([m[1] for m in mods])
+    mgs = torch.cat([m[2] for m in mods])
+    ws_h = ws0.clone()
+    n4, k4 = wc.shape[0], cfg["x"][2]
+    y4 = torch.empty((T4, n4), dtype=torch.bfloat16, device=dev)
+
+    def harm(_r):
+        ws_h.copy_(ws0)
+        nv.harmonize_fused_scales(ws_h, mgs, rows4, k4)
+
+    th = _timed(torch, np, stream, harm, 10)
+    tcopy = _timed(torch, np, stream, lambda r: ws_h.copy_(ws0), 10)
+    shared, _ = nv.harmonize_fused_scales(ws_h, mgs, rows4, k4)
+    fl4 = 2.0 * T4 * n4 * k4
+    variants = {
+        "naive_fused": lambda r: nv.gemm(*a4, wc, ws0, mgs[0:1], out_dtype=torch.bfloat16, out=y4),
+        "harmonized_fused": lambda r: nv.gemm(*a4, wc, ws_h, shared, out_dtype=torch.bfloat16, out=y4),
+        "segmented": lambda r: nv.gemm_segmented(*a4, wc, ws0, mgs, rows4, out_dtype=torch.bfloat16, out=y4),
+    }
+    per_mod_out = [torch.empty((T4, m[0].shape[0]), dtype=torch.bfloat16, device=dev) for m in mods]
+
+    def per_module(_r):
+        for m, yo in zip(mods, per_mod_out):
+            nv.gemm(*a4, *m, out_dtype=torch.bfloat16, out=yo)
+
+    variants["per_module_4_gemms"] = per_module
+    fused = {"harmonize_ms_p10_p50_p90": _pcts(np, [max(a - b, 0.0) for a, b in zip(sorted(th), sorted(tcopy))]),
+             "harmonize_bytes": int(ws0.numel()),
+             "note": "harmonize time = (scale copy + harmonize) - scale copy, offline work"}
+    for name, fn in variants.items():
+        t = _timed(torch, np, stream, fn, 10)
+        fused[name] = {"ms_p10_p50_p90": _pcts(np, t),
+                       "tflops": round(fl4 / (float(np.median(t)) * 1e-3) / 1e12, 1),
+                       "frac_of_peak": round(fl4 / (float(np.median(t)) * 1e-3) / 1e12 / PEAK_FP16_MFMA_TFLOPS, 4)}
+    res["fused_gdn"] = {"shape": f"{T4} x {n4} x {k4} (qkv 8192 | z 4096 | a 48 | b 48)", **fused}
+    del x4, a4, mods, wc, ws0, ws_h, y4, per_mod_out
+    torch.cuda.empty_cache()
+    return res
 
 
 def extra_measurements(nv, torch, np, dev, stream, xs, calib, qbuf, ys, in_codes, in_scales, in_gs, in_scales_modules,

@@ -20,6 +20,11 @@ from dataclasses import dataclass
 import torch
 
 HIDDEN = 5120
+# Magnitude of the lognormal workload's outlier channel: with one constant
+# channel of magnitude R among C = 5120 unit-RMS ones the kurtosis is about
+# R^4 / (C (1 + R^2 / C)^2), ~1.5e3 at R = 76, the level the pages report
+# for the median layer (LIT-800, "Key takeaways", block-scaling bullet).
+OUTLIER_MAGNITUDE = 76.0
 
 
 @dataclass(frozen=True)
@@ -54,7 +59,11 @@ def activations(kind: str, rows: int, cols: int, seed: int, device="cpu",
       "gauss_outlier2"  N(0,1) with 2 random channels scaled x50
       "t3_outlier1pct"  Student-t(3) with 1% of channels scaled x60
       "lognormal_rms"   per-channel RMS exp(1.5 z) times N(0,1), plus one
-                        outlier channel at 53x the tensor RMS (kurtosis ~1.5e3)
+                        outlier channel of constant magnitude 76 (random
+                        sign) against the base tensor RMS of 1: kurtosis
+                        ~1.4e3-1.5e3 and max/RMS ~50-65 at widths 4096 and
+                        5120; at width 17408 the largest lognormal channel
+                        (more channels, a longer tail) sets max/RMS ~127
     Rows are drawn in chunks from one seeded stream so large tensors never
     need a second full-size temporary.
     """
@@ -73,7 +82,6 @@ def activations(kind: str, rows: int, cols: int, seed: int, device="cpu",
         rms = torch.exp(1.5 * torch.randn(cols, generator=cgen))
         rms = rms / torch.sqrt(torch.mean(rms * rms))          # tensor RMS 1
         ch = torch.randperm(cols, generator=cgen)[:1]
-        rms[ch] = 53.0
         mult = rms
     else:
         raise ValueError(f"unknown activation kind {kind!r}")
@@ -84,7 +92,11 @@ def activations(kind: str, rows: int, cols: int, seed: int, device="cpu",
             v = _student_t3((r1 - r0, cols), gen, device)
         else:
             v = torch.randn((r1 - r0, cols), generator=gen, device=device, dtype=torch.float32)
-        out[r0:r1] = (v * mult).to(dtype)
+        v = v * mult
+        if kind == "lognormal_rms":
+            # a "massive activation" channel: constant magnitude, random sign
+            v[:, ch.to(device)] = OUTLIER_MAGNITUDE * torch.sign(v[:, ch.to(device)])
+        out[r0:r1] = v.to(dtype)
     return out
 
 
@@ -149,7 +161,7 @@ CONFIGS = {
         "desc": "one hybrid layer at 32768 tokens: GDN qkv/z/a/b fused in-projection "
                 "[12384x5120], out [5120x4096], MLP gate/up [34816x5120], down [5120x17408]; "
                 "inputs [32768 x {5120,4096,17408}] bf16 with lognormal per-channel RMS "
-                "(sigma 1.5) and one 53x outlier channel; seed 4",
+                "(sigma 1.5) and one constant-magnitude 76x outlier channel; seed 4",
         "rows": 32768,
         "x": ("lognormal_rms", 32768, HIDDEN, torch.bfloat16),
         "projections": [ProjectionSpec("qkv", 8192, HIDDEN, 0.02),
