@@ -826,6 +826,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     }
   }
   {
+    const bool full_tile = vec_ok && m0 + BM <= M && n0 + BN <= N;
     uint8_t* strip = smem + STAGES * kStageBytes + wave * kStripBytes;
     constexpr int kChunksPerRow = kStripCols * kEsz / 16;
     constexpr int kChunkElems = 16 / kEsz;
@@ -869,19 +870,31 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
           const int id = q * 64 + lane;
           d[q] = *reinterpret_cast<const u32x4_t*>(strip + (id / kChunksPerRow) * kStripRow + (id % kChunksPerRow) * 16);
         }
+        if (full_tile) {
+          // the whole tile lies inside the output: unconditional 16-byte
+          // stores (a uniform branch; no per-lane bound checks)
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) {
-          const int id = q * 64 + lane;
-          const int r = id / kChunksPerRow, c = id % kChunksPerRow;
-          const int grow = grow0 + r, gcol = gcol0 + c * kChunkElems;
-          if (grow < M) {
-            out_t* dst = reinterpret_cast<out_t*>(y) + (int64_t)grow * ldy + gcol;
-            if (vec_ok && gcol + kChunkElems <= N) {
-              __builtin_nontemporal_store(d[q], reinterpret_cast<u32x4_t*>(dst));
-            } else {
-              const out_t* e = reinterpret_cast<const out_t*>(&d[q]);
-              for (int t = 0; t < kChunkElems; ++t)
-                if (gcol + t < N) dst[t] = e[t];
+          for (int q = 0; q < kQ; ++q) {
+            const int id = q * 64 + lane;
+            const int r = id / kChunksPerRow, c = id % kChunksPerRow;
+            out_t* dst = reinterpret_cast<out_t*>(y) + (int64_t)(grow0 + r) * ldy + gcol0 + c * kChunkElems;
+            __builtin_nontemporal_store(d[q], reinterpret_cast<u32x4_t*>(dst));
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < kQ; ++q) {
+            const int id = q * 64 + lane;
+            const int r = id / kChunksPerRow, c = id % kChunksPerRow;
+            const int grow = grow0 + r, gcol = gcol0 + c * kChunkElems;
+            if (grow < M) {
+              out_t* dst = reinterpret_cast<out_t*>(y) + (int64_t)grow * ldy + gcol;
+              if (vec_ok && gcol + kChunkElems <= N) {
+                __builtin_nontemporal_store(d[q], reinterpret_cast<u32x4_t*>(dst));
+              } else {
+                const out_t* e = reinterpret_cast<const out_t*>(&d[q]);
+                for (int t = 0; t < kChunkElems; ++t)
+                  if (gcol + t < N) dst[t] = e[t];
+              }
             }
           }
         }
