@@ -75,38 +75,72 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   scales[b] = (uint8_t)s;
 }
 
+// 16-byte chunk c of the tensor (8 bf16 or 4 fp32 values; chunks_per_row
+// per row of ldx values).
+template <bool kBf16, bool kContig>
+__device__ __forceinline__ u32x4_t amax_chunk(const void* x, int64_t c, int64_t chunks_per_row, int64_t ldx) {
+  constexpr int kPer = kBf16 ? 8 : 4;  // values per 16-byte chunk
+  int64_t off;
+  if constexpr (kContig) {
+    off = c * kPer;
+  } else {
+    const int64_t row = c / chunks_per_row;
+    off = row * ldx + (c - row * chunks_per_row) * kPer;
+  }
+  const int64_t byte_off = off * (kBf16 ? 2 : 4);
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(x) + byte_off));
+}
+
+template <bool kBf16>
+__device__ __forceinline__ float amax_fold(float m, u32x4_t t) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (kBf16) {
+      m = fmaxf(m, fabsf(__uint_as_float(t[i] << 16)));
+      m = fmaxf(m, fabsf(__uint_as_float(t[i] & 0xFFFF0000u)));
+    } else {
+      m = fmaxf(m, fabsf(__uint_as_float(t[i])));
+    }
+  }
+  return m;
+}
+
+constexpr int kAmaxUnroll = 4;
+// At most 1024 workgroups (4 per CU), each streaming many windows: on the
+// layer inputs (32768 x 4096 .. 17408 bf16) this read 5.6-6.8 TB/s, against
+// 4.2-6.7 with 4096 workgroups and 5.3-6.8 with 512 x 8 or 1024 x 2 chunks
+// per lane per pass.
+constexpr int64_t kAmaxMaxGroups = 1024;
+
 // Absolute maximum of the tensor into *amax_bits (float bits; all values
 // non-negative, so unsigned max == float max).  *amax_bits starts at 0.
+// Each pass of a workgroup reads one contiguous window of kAmaxUnroll x
+// kThreads chunks (lane l: chunks l, l + kThreads, ...), all loads issued
+// before the first max, so every lane keeps kAmaxUnroll loads in flight;
+// the windows stride over the tensor by the grid.  The
+// workgroup's maximum goes to *amax_bits with one atomic, and only if it
+// exceeds the value already there (read first; the maximum only grows, so a
+// skipped value is never the result): the atomics of all workgroups land on
+// one address and queue there.  Against one atomic per workgroup and one
+// chunk per lane per pass, this cut the amax pass from 75-95 us to 46-60 us
+// on 32768 x {4096, 5120} bf16 inputs and from 194 to 170 us on 32768 x 17408.
 template <bool kBf16, bool kContig>
 __global__ __launch_bounds__(kThreads) void amax_kernel(const void* __restrict__ x, int64_t nchunks,
                                                         int64_t chunks_per_row, int64_t ldx,
                                                         uint32_t* __restrict__ amax_bits) {
-  constexpr int kPer = kBf16 ? 8 : 4;  // values per 16-byte chunk
+  constexpr int64_t kWin = (int64_t)kAmaxUnroll * kThreads;
   float m = 0.0f;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nchunks; c += stride) {
-    int64_t off;
-    if constexpr (kContig) {
-      off = c * kPer;
-    } else {
-      const int64_t row = c / chunks_per_row;
-      off = row * ldx + (c - row * chunks_per_row) * kPer;
-    }
-    if constexpr (kBf16) {
-      const u32x4_t t = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(x) + off));
-      const uint32_t w[4] = {t[0], t[1], t[2], t[3]};
+  const int64_t step = (int64_t)gridDim.x * kWin;
+  int64_t c = (int64_t)blockIdx.x * kWin + threadIdx.x;
+  for (; c + (kAmaxUnroll - 1) * kThreads < nchunks; c += step) {
+    u32x4_t t[kAmaxUnroll];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        m = fmaxf(m, fabsf(__uint_as_float(w[i] << 16)));
-        m = fmaxf(m, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
-      }
-    } else {
-      const floatx4_t t = __builtin_nontemporal_load(
-          reinterpret_cast<const floatx4_t*>(reinterpret_cast<const float*>(x) + off));
-      m = fmaxf(fmaxf(m, fabsf(t[0])), fmaxf(fabsf(t[1]), fmaxf(fabsf(t[2]), fabsf(t[3]))));
-    }
+    for (int u = 0; u < kAmaxUnroll; ++u) t[u] = amax_chunk<kBf16, kContig>(x, c + u * kThreads, chunks_per_row, ldx);
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) m = amax_fold<kBf16>(m, t[u]);
   }
+  // the last, partial window: this lane's chunks of it that exist
+  for (; c < nchunks; c += kThreads) m = amax_fold<kBf16>(m, amax_chunk<kBf16, kContig>(x, c, chunks_per_row, ldx));
   // wave reduction, then one value per wave through LDS
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   __shared__ float part[kThreads / 64];
@@ -116,7 +150,9 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const void* __restrict__
   if (threadIdx.x == 0) {
     float r = part[0];
     for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, part[i]);
-    atomicMax(amax_bits, __float_as_uint(r));
+    const uint32_t rb = __float_as_uint(r);
+    if (rb > __hip_atomic_load(amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(amax_bits, rb);
   }
 }
 
@@ -135,8 +171,8 @@ hipError_t launch_typed(const void* x, int64_t rows, int64_t cols, int64_t ldx, 
       const int per = kBf16 ? 8 : 4;
       const int64_t cpr = cols / per;
       const int64_t nchunks = rows * cpr;
-      int64_t grid = (nchunks + kThreads * 4 - 1) / (kThreads * 4);
-      if (grid > 256 * 16) grid = 256 * 16;
+      int64_t grid = (nchunks + kThreads * kAmaxUnroll - 1) / (kThreads * kAmaxUnroll);
+      if (grid > kAmaxMaxGroups) grid = kAmaxMaxGroups;
       if (grid < 1) grid = 1;
       amax_kernel<kBf16, kContig><<<(unsigned)grid, kThreads, 0, stream>>>(
           x, nchunks, cpr, ldx, reinterpret_cast<uint32_t*>(gs));
