@@ -55,6 +55,53 @@ def test_harmonize_power_of_two_ratios_exact():
     assert np.array_equal(got, want)
 
 
+def _harmonize_bytes(scales_np, gs, rows, k, offset=0):
+    """GPU harmonize of a flat byte buffer placed `offset` bytes into its
+    allocation (offset 1: a misaligned buffer, taken byte by byte)."""
+    buf = torch.zeros(scales_np.size + 16, dtype=torch.uint8, device="cuda")
+    view = buf[offset:offset + scales_np.size]
+    view.copy_(torch.from_numpy(np.ascontiguousarray(scales_np).reshape(-1)))
+    shared, counters = nv.harmonize_fused_scales(view, torch.tensor(gs, dtype=torch.float32, device="cuda"),
+                                                 rows, k)
+    torch.cuda.synchronize()
+    out = buf.cpu().numpy()
+    assert not out[:offset].any() and not out[offset + scales_np.size:].any(), "wrote outside the buffer"
+    return out[offset:offset + scales_np.size], float(shared.item()), counters.cpu().numpy().astype(np.int64)
+
+
+@pytest.mark.parametrize("offset", [0, 1])
+def test_harmonize_every_scale_byte_of_every_module(offset):
+    # one row per module holding every E4M3 scale byte 0x00..0x7E, so every
+    # (scale, module) pair of the kernel's lookup table is checked
+    need_gpu()
+    gs = [np.float32(v) for v in (0.0123, 0.5, 3.7e-3, 1.0, 7.25e-5)]
+    rows = [1] * len(gs)
+    k = 16 * 127
+    mods = [np.arange(127, dtype=np.uint8).reshape(1, 127) for _ in gs]
+    got, g_star, counters = _harmonize_bytes(np.concatenate(mods), gs, rows, k, offset)
+    want, w_star, n_inexact, n_sub = ref.harmonize_ref(mods, gs)
+    assert g_star == float(w_star)
+    assert np.array_equal(got, want.reshape(-1))
+    assert counters[0] == n_inexact and counters[1] == n_sub
+
+
+@pytest.mark.parametrize("offset", [0, 1])
+def test_harmonize_ragged_rows_and_module_ends_inside_chunks(offset):
+    # 17 scales per row, so 16-byte chunks straddle rows and module ends; an
+    # empty module; random scale bytes
+    need_gpu()
+    rng = np.random.default_rng(5 + offset)
+    rows = [5, 0, 3, 7, 1, 40]
+    gs = [np.float32(v) for v in (0.02, 0.3, 0.02, 1.5e-3, 4.0, 0.25)]
+    k = 16 * 17
+    mods = [rng.integers(0, 0x7F, size=(r, 17)).astype(np.uint8) for r in rows]
+    got, g_star, counters = _harmonize_bytes(np.concatenate(mods), gs, rows, k, offset)
+    want, w_star, n_inexact, n_sub = ref.harmonize_ref(mods, gs)
+    assert g_star == float(w_star)
+    assert np.array_equal(got, want.reshape(-1))
+    assert counters[0] == n_inexact and counters[1] == n_sub
+
+
 def test_fused_gdn_fused_variants():
     """C4: naive fused, harmonized fused and segmented epilogue against their
     oracles on every output element (4096 tokens x 12384 columns), and
