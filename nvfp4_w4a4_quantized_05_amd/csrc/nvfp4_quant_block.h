@@ -46,10 +46,12 @@ namespace {
 // (int)bits(d) + odd > 0 means d > 0, or d == +0 and s0 odd.
 __device__ __forceinline__ uint32_t exact_scale(uint32_t s0, float v0, float bm, float g) {
   const uint32_t odd = s0 & 1u;
-  const float lo = 0.5f * (e4m3_to_f32(s0 - 1) + v0);  // exact; NaN for s0 = 0 (unused)
-  const float hi = 0.5f * (v0 + e4m3_to_f32(s0 + 1));  // exact; NaN for s0 = 0x7E (unused)
-  const int dl = (int)(__float_as_uint(fmaf(lo * 6.0f, g, -bm)) + odd);  // > 0: round down
-  const int du = (int)(__float_as_uint(fmaf(hi * 6.0f, g, -bm)) - odd);  // < 0: round up
+  // 6 x the midpoints below and above s0: 3 x (sum of two neighbouring E4M3
+  // values), exact (at most 7 significant bits); NaN for s0 = 0 / 0x7E (unused)
+  const float lo6 = 3.0f * (e4m3_to_f32(s0 - 1) + v0);
+  const float hi6 = 3.0f * (v0 + e4m3_to_f32(s0 + 1));
+  const int dl = (int)(__float_as_uint(fmaf(lo6, g, -bm)) + odd);  // > 0: round down
+  const int du = (int)(__float_as_uint(fmaf(hi6, g, -bm)) - odd);  // < 0: round up
   uint32_t s = s0;
   s = (s0 > 0u && dl > 0) ? s0 - 1 : s;
   s = (s0 < 0x7Eu && du < 0) ? s0 + 1 : s;
@@ -57,22 +59,23 @@ __device__ __forceinline__ uint32_t exact_scale(uint32_t s0, float v0, float bm,
 }
 
 // Settled quotient for a value x with approximate quotient y: m = y rounded
-// to 2 mantissa bits (ties away from zero); with unit val(s) g: beyond m
-// (|x| > |m| val(s) g) the result is |m| moved away from zero, short of it
-// toward zero, and on a tie toward the even code: of the E2M1 decision
+// to 2 mantissa bits (ties away from zero), sign kept; with unit val(s) g:
+// beyond m (|x| > |m| val(s) g) the result is m moved away from zero, short
+// of it toward zero, and on a tie toward the even code: of the E2M1 decision
 // points 0.25 | 0.75 | 1.25 | 1.75 | 2.5 | 3.5 | 5, exactly those with the
 // first mantissa bit set (0.75, 1.75, 3.5) have an odd code below them.  So
-// with d = the exact difference m val(s) g - |x| (never -0: the product is
+// with d = the exact difference |m| val(s) g - |x| (never -0: the product is
 // >= 0) and b = that mantissa bit of m, "round down" is d > 0, or d = +0
-// and b = 0, i.e. (int)bits(d) >= b.  The sign is y's (also for y = -0).
-// m = 0 stays 0.
+// and b = 0, i.e. (int)bits(d) >= b.  Moving m by 2^-8 of itself keeps its
+// sign, which is y's (also for y = -0); m = +-0 stays +-0.
 __device__ __forceinline__ float settle_e2m1(float y, float ax, float sval, float g) {
-  const uint32_t mb = (__float_as_uint(y) + 0x100000u) & 0x7FE00000u;  // |m|
+  const uint32_t mb = (__float_as_uint(y) + 0x100000u) & 0xFFE00000u;  // m, sign kept
   const float m = __uint_as_float(mb);
   const int b = (int)((mb >> 22) & 1u);
-  const bool down = (int)__float_as_uint(fmaf(m * sval, g, -ax)) >= b;
-  const float r = fmaf(m, down ? -0x1p-8f : 0x1p-8f, m);
-  return __uint_as_float((__float_as_uint(r) & 0x7FFFFFFFu) | (__float_as_uint(y) & 0x80000000u));
+  const bool down = (int)__float_as_uint(fmaf(fabsf(m) * sval, g, -ax)) >= b;
+  // a product, not m + m k: (1 -/+ 2^-8) m is exact (at most 12 significant
+  // bits) and keeps the sign of m = -0
+  return m * (down ? 1.0f - 0x1p-8f : 1.0f + 0x1p-8f);
 }
 
 // Quantize the 16 values v of one block with tensor scale g (r6 = approximate
