@@ -1033,12 +1033,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     u32x4_t w[2 * NB];
     u32x4_t a[2 * MB16];
   };
-  // Tile t0 + t of this wave.  Tiles past the wave's range (t >= nt) are
-  // read at an offset beyond every buffer's size: the loads return zeros
-  // without touching memory, and the zero tile adds nothing to the sums.
-  // That keeps the main loop branch-free, so the compiler can wait for each
-  // tile individually instead of draining every load in flight.
-  constexpr uint32_t kOutside = 0x80000000u;  // > any buffer size used here
+  // Tile t0 + t of this wave.  The tile's offset in the rows is the
+  // wave-uniform SGPR offset of the loads, so the per-lane offsets stay
+  // fixed and no vector instruction addresses a tile.  Tiles past the wave's
+  // range (t >= nt) are read through resources of size 0 (a uniform select
+  // of SGPRs): the loads return zeros without touching memory, and the zero
+  // tile adds nothing to the sums.  That keeps the main loop branch-free,
+  // so the compiler can wait for each tile individually instead of draining
+  // every load in flight.
+  const __amdgpu_buffer_rsrc_t rw_none = make_rsrc(w_codes, 0), ra_none = make_rsrc(a_codes, 0);
   auto load = [&](Tile& T, int t) {
     const bool ok = t < nt;
     const uint32_t kc = (uint32_t)(t0 + t) * kTileBytes;
@@ -1050,13 +1053,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
       T.x[0] = p[0];
       T.x[1] = p[1];
     }
+    const __amdgpu_buffer_rsrc_t rwt = ok ? rw : rw_none;
 #pragma unroll
-    for (int i = 0; i < 2 * NB; ++i)
-      T.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? w_off[i] + kc : kOutside, 0, 0);
+    for (int i = 0; i < 2 * NB; ++i) T.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rwt, w_off[i], kc, 0);
     if constexpr (kXIn == 0) {
+      const __amdgpu_buffer_rsrc_t rat = ok ? ra : ra_none;
 #pragma unroll
-      for (int i = 0; i < 2 * MB16; ++i)
-        T.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off[i] + kc : kOutside, 0, 0);
+      for (int i = 0; i < 2 * MB16; ++i) T.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rat, a_off[i], kc, 0);
     }
   };
 
