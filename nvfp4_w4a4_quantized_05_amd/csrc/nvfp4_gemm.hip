@@ -919,15 +919,14 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
 // values.  Codes go straight into registers, D tiles ahead; only the scale
 // bytes and the final reduction use LDS.
 //
-//  * One code load reads 8 rows x 128 contiguous bytes (lane L: row L % 8,
-//    16-byte chunk L / 8), the pattern that reaches full HBM read bandwidth;
-//    16 rows x 64 bytes per instruction loses about a quarter of it.
 //  * v_mfma_f32_16x16x32_f16 wants lane L to hold row L % 16 of its 16-row
-//    block.  Two loads X (rows 0-7) and Y (rows 8-15) are turned into that
-//    layout with two DPP row shifts by 8 lanes: R0 = X in lanes 0-7 of every
-//    16-lane row and Y shifted up in lanes 8-15 (chunk 2g for lane group g),
-//    R1 = X shifted down in lanes 0-7 and Y in lanes 8-15 (chunk 2g + 1).
-//    A is loaded and rearranged the same way (it stays in L2).
+//    block.  The code loads deliver that layout directly: load h (0 or 1) of
+//    a block gives lane L row L % 16, 16-byte chunk 2 (L / 16) + h of the
+//    tile, so a lane group g of 16 lanes holds chunks 2g and 2g + 1.  The
+//    two loads of a block read the halves of the same 128-byte row pieces.
+//    (Loads of 8 rows x 128 contiguous bytes, turned into this layout with
+//    two DPP row shifts per dword, took 60 more VALU per tile and measured
+//    1-4% slower at every M.)  A is loaded the same way (it stays in L2).
 //  * The scale bytes of the wave's whole K range (16 bytes per row per tile)
 //    are copied to LDS once, up front, in contiguous runs per row; read per
 //    tile, they cost no extra memory requests.
@@ -1021,12 +1020,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
 
   // per-lane code offsets at tile 0 of this wave's K range
   uint32_t w_off[2 * NB], a_off[2 * MB16];
+  // load i: block i / 2, all 16 rows (lane L: row L % 16) x 16-byte chunk
+  // 2 (L / 16) + i % 2 of the tile (the MFMA operand layout)
 #pragma unroll
-  for (int i = 0; i < 2 * NB; ++i)  // block i / 2, rows 8 (i % 2) .. + 7
-    w_off[i] = (uint32_t)(n0 + 8 * i + (lane & 7)) * row_bytes + (uint32_t)(lane >> 3) * 16;
+  for (int i = 0; i < 2 * NB; ++i)
+    w_off[i] = (uint32_t)(n0 + 16 * (i / 2) + (lane & 15)) * row_bytes + (uint32_t)(2 * (lane >> 4) + i % 2) * 16;
 #pragma unroll
   for (int i = 0; i < 2 * MB16; ++i)
-    a_off[i] = (uint32_t)(8 * i + (lane & 7)) * row_bytes + (uint32_t)(lane >> 3) * 16;
+    a_off[i] = (uint32_t)(16 * (i / 2) + (lane & 15)) * row_bytes + (uint32_t)(2 * (lane >> 4) + i % 2) * 16;
 
   struct Tile {
     u32x4_t x[kXIn ? 2 : 1];  // kXIn: the lane's 16 bf16 values
@@ -1075,16 +1076,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[j][b][v] = 0.0f;
 
-  // X (rows 0-7) and Y (rows 8-15) of a 16-row block -> lane q holds row q:
-  // r0 = chunk 2g, r1 = chunk 2g + 1 of the tile.
-  auto to_mfma_rows = [](const u32x4_t& X, const u32x4_t& Y, u32x4_t& r0, u32x4_t& r1) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      r0[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)X[d], (int)Y[d], 0x118, 0xF, 0xC, false);  // row_shr:8 -> lanes 8-15
-      r1[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)Y[d], (int)X[d], 0x108, 0xF, 0x3, false);  // row_shl:8 -> lanes 0-7
-    }
-  };
-
   // dequantized MFMA operands of the last three steps (see compute)
   half8_t wv[3][NB], av[3][MB16];
   auto compute = [&](const Tile& T, int t) {
@@ -1122,12 +1113,19 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     for (int j = 0; j < NB; ++j) wsd[j] = *reinterpret_cast<const uint32_t*>(wsl + (16 * j + q) * run + ts);
 #pragma unroll
     for (int b = 0; b < MB16; ++b) asd[b] = *reinterpret_cast<const uint32_t*>(asl + (16 * b + q) * run + ts);
+    // operands: chunks 2g (index 0) and 2g + 1 (index 1) of the lane's row
     u32x4_t wr[NB][2], ar[MB16][2];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) to_mfma_rows(T.w[2 * j], T.w[2 * j + 1], wr[j][0], wr[j][1]);
+    for (int j = 0; j < NB; ++j) {
+      wr[j][0] = T.w[2 * j];
+      wr[j][1] = T.w[2 * j + 1];
+    }
     if constexpr (kXIn == 0) {
 #pragma unroll
-      for (int b = 0; b < MB16; ++b) to_mfma_rows(T.a[2 * b], T.a[2 * b + 1], ar[b][0], ar[b][1]);
+      for (int b = 0; b < MB16; ++b) {
+        ar[b][0] = T.a[2 * b];
+        ar[b][1] = T.a[2 * b + 1];
+      }
     } else {
       // A already in LDS: row q, chunks 2g and 2g + 1 of the tile
       const int tc = min(t, nt - 1) * kTileBytes + 32 * g;
