@@ -72,7 +72,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   out[0] = w0;
   out[1] = w1;
   __builtin_nontemporal_store(out, reinterpret_cast<u32x2_t*>(codes) + b);
-  scales[b] = (uint8_t)s;
+  // streaming stores for both (plain code stores measured 3-4% slower,
+  // plain scale stores 1-2% slower)
+  __builtin_nontemporal_store((uint8_t)s, scales + b);
 }
 
 // 16-byte chunk c of the tensor (8 bf16 or 4 fp32 values; chunks_per_row
