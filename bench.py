@@ -527,7 +527,7 @@ def config_measurements(nv, torch, np, dev, stream):
         wq = nv.quantize(normal_weights(p.n, p.k, p.std, seed=cfg["seed"] * 100 + i, device=dev))
         yk = torch.empty((T, p.n), dtype=torch.bfloat16, device=dev)
         tq = _timed(torch, np, stream, lambda r, xk=xk, g=g, a=a: nv.quantize(xk, g, from_amax=False, codes=a[0],
-                                                                              scales=a[1]), 10)
+                                                                              scales=a[1]), 10, per_batch=20)
         tg = _timed(torch, np, stream, lambda r, a=a, wq=wq, yk=yk: nv.gemm(*a, *wq, out_dtype=torch.bfloat16,
                                                                             out=yk), 10)
         fl = 2.0 * T * p.n * p.k
@@ -561,8 +561,8 @@ def config_measurements(nv, torch, np, dev, stream):
         ws_h.copy_(ws0)
         nv.harmonize_fused_scales(ws_h, mgs, rows4, k4)
 
-    th = _timed(torch, np, stream, harm, 10)
-    tcopy = _timed(torch, np, stream, lambda r: ws_h.copy_(ws0), 10)
+    th = _timed(torch, np, stream, harm, 10, per_batch=20)
+    tcopy = _timed(torch, np, stream, lambda r: ws_h.copy_(ws0), 10, per_batch=20)
     shared, _ = nv.harmonize_fused_scales(ws_h, mgs, rows4, k4)
     fl4 = 2.0 * T4 * n4 * k4
     variants = {
@@ -581,7 +581,7 @@ def config_measurements(nv, torch, np, dev, stream):
              "harmonize_bytes": int(ws0.numel()),
              "note": "harmonize time = (scale copy + harmonize) - scale copy, offline work"}
     for name, fn in variants.items():
-        t = _timed(torch, np, stream, fn, 10)
+        t = _timed(torch, np, stream, fn, 10, per_batch=5)
         fused[name] = {"ms_p10_p50_p90": _pcts(np, t),
                        "tflops": round(fl4 / (float(np.median(t)) * 1e-3) / 1e12, 1),
                        "frac_of_peak": round(fl4 / (float(np.median(t)) * 1e-3) / 1e12 / PEAK_FP16_MFMA_TFLOPS, 4)}
