@@ -115,13 +115,23 @@ NVFP4_API nvfp4_status_t nvfp4_quantize(const void* x, int32_t in_dtype, int64_t
  *   M, N, K            M >= 0, N > 0, K > 0, K % 16 == 0
  *   y                  device out, [M x ldy] of `out_dtype` (NVFP4_OUT_F32 or
  *                      NVFP4_OUT_BF16, round-to-nearest-even); ldy >= N
- *   workspace          device scratch or NULL; nvfp4_gemm_workspace_size()
- *                      bytes are required (0 for every shape today)
+ *   workspace          device scratch, 16-byte aligned, owned by the caller
+ *                      (NULL when nvfp4_gemm_workspace_size() is 0); at least
+ *                      nvfp4_gemm_workspace_size(M, N, K, out_dtype) bytes
+ *                      are required, else NVFP4_ERR_WORKSPACE.  Its contents
+ *                      need no initialisation and are overwritten.  Calls
+ *                      that share one workspace must be ordered (one stream).
  * Fast path: K % 128 == 0 and codes/scales base pointers 16-/8-byte aligned;
  * other K % 16 == 0 shapes take a slower generic kernel with the same result.
  * Accuracy: |y - Y| <= 1e-4 * sum_k |a_k w_k| against the exact product for
  * fp32 output (plus half a bf16 ulp of Y for bf16 output).  Deterministic:
  * the same inputs give bit-identical output.
+ * Tail split: the fast path gives each workgroup a 256 x 256 output tile, one
+ * per CU at a time.  When the tile count leaves the last round of 256 at most
+ * a quarter full (4096 x 12384 has 784 tiles: 3 rounds and 16 tiles), each
+ * of those last tiles is split over K into 2-8 parts computed side by side;
+ * their fp32 partial sums go to the workspace and a second kernel adds them
+ * in part order, scales and writes them.  Only these shapes need a workspace.
  */
 NVFP4_API nvfp4_status_t nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
@@ -181,6 +191,8 @@ NVFP4_API nvfp4_status_t nvfp4_gemm_segmented(const uint8_t* a_codes, const uint
  *                  may be NULL when decay_module is -1
  *   write_module   index of the write-strength module (the b projection),
  *                  or -1; different from decay_module unless both are -1
+ * The gated epilogue never splits tiles, so this call needs no workspace
+ * (workspace may be NULL and workspace_bytes 0).
  * NVFP4_ERR_SHAPE for a module index outside -1 .. n_modules - 1 or equal
  * indices; NVFP4_ERR_NULL / NVFP4_ERR_ALIGN (4 bytes) for the gate
  * parameters; other errors as for nvfp4_gemm_segmented.  Accuracy: the
@@ -389,7 +401,11 @@ NVFP4_API nvfp4_status_t nvfp4_harmonize_fused_scales(uint8_t* scales, const flo
                                             int64_t K, float* shared_gs, uint32_t* counters,
                                             void* stream);
 
-/* Bytes of workspace nvfp4_gemm needs for this shape (0 today). */
+/* Bytes of workspace nvfp4_gemm and nvfp4_gemm_segmented need for this
+ * shape: the partial sums of the split tail tiles (256 KiB per tile and
+ * part), 0 for every shape without a tail split (out_dtype does not change
+ * it).  4096 x 12384 x 5120 needs 32 MiB; the 32K-token projections, the
+ * decode shapes and the small shapes need none. */
 NVFP4_API size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t out_dtype);
 
 /* Static description of a status code; never NULL. */

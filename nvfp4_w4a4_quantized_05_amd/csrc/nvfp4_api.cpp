@@ -26,7 +26,7 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 nvfp4_status_t gemm_checked(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
                             const uint8_t* w_codes, const uint8_t* w_scales, const nvfp4::ColScales& cs,
                             int64_t M, int64_t N, int64_t K, void* y, int32_t out_dtype, int64_t ldy,
-                            size_t workspace_bytes, void* stream) {
+                            void* workspace, size_t workspace_bytes, void* stream) {
   if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_DTYPE;
   if (M < 0 || N <= 0 || K <= 0 || K % 16 != 0 || ldy < N) return NVFP4_ERR_SHAPE;
   if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return NVFP4_ERR_SHAPE;
@@ -34,11 +34,17 @@ nvfp4_status_t gemm_checked(const uint8_t* a_codes, const uint8_t* a_scales, con
   if (!a_codes || !a_scales || !a_gs || !w_codes || !w_scales || !cs.gs || !y) return NVFP4_ERR_NULL;
   if (!aligned(a_gs, 4) || !aligned(cs.gs, 4) || !aligned(y, out_dtype == NVFP4_OUT_BF16 ? 2 : 4))
     return NVFP4_ERR_ALIGN;
-  if (workspace_bytes < nvfp4_gemm_workspace_size(M, N, K, out_dtype)) return NVFP4_ERR_WORKSPACE;
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   if (tiles > (int64_t)INT_MAX) return NVFP4_ERR_SHAPE;
+  // the gate epilogue never splits tiles, so it takes no workspace
+  const bool gates = cs.decay_hi > cs.decay_lo || cs.write_hi > cs.write_lo;
+  const size_t need = gates ? 0 : nvfp4::gemm_split_workspace_bytes(M, N, K);
+  if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+  if (need > 0 && !workspace) return NVFP4_ERR_NULL;
+  if (need > 0 && !aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
   return hip_status(nvfp4::launch_gemm(a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y,
-                                       out_dtype == NVFP4_OUT_BF16, ldy, (hipStream_t)stream));
+                                       out_dtype == NVFP4_OUT_BF16, ldy, (hipStream_t)stream,
+                                       need > 0 ? workspace : nullptr, need));
 }
 
 
@@ -122,8 +128,9 @@ nvfp4_status_t nvfp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int
 }
 
 size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t out_dtype) {
-  (void)M; (void)N; (void)K; (void)out_dtype;
-  return 0;
+  (void)out_dtype;
+  if (M <= 0 || N <= 0 || K <= 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return 0;
+  return nvfp4::gemm_split_workspace_bytes(M, N, K);
 }
 
 nvfp4_status_t nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
@@ -136,7 +143,7 @@ nvfp4_status_t nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
     cs.n = 1;
     cs.end[0] = (N > 0 && N <= INT_MAX) ? (int)N : 0;  // out-of-range N fails the shape check
     return gemm_checked(a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y, out_dtype, ldy,
-                        workspace_bytes, stream);
+                        workspace, workspace_bytes, stream);
   } catch (...) {
     return NVFP4_ERR_HIP;
   }
@@ -160,7 +167,7 @@ nvfp4_status_t nvfp4_gemm_segmented(const uint8_t* a_codes, const uint8_t* a_sca
       cs.end[i] = (int)N;
     }
     return gemm_checked(a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y, out_dtype, ldy,
-                        workspace_bytes, stream);
+                        workspace, workspace_bytes, stream);
   } catch (...) {
     return NVFP4_ERR_HIP;
   }
@@ -196,7 +203,7 @@ nvfp4_status_t nvfp4_gemm_segmented_gates(const uint8_t* a_codes, const uint8_t*
     cs.a_log = a_log;
     cs.dt_bias = dt_bias;
     return gemm_checked(a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y, out_dtype, ldy,
-                        workspace_bytes, stream);
+                        workspace, workspace_bytes, stream);
   } catch (...) {
     return NVFP4_ERR_HIP;
   }

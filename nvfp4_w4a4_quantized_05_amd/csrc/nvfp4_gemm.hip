@@ -27,6 +27,7 @@
 //    always sit inside one 16-value block, i.e. one scale.
 //  * The RN32(g_a g_w) multiply and the fp32 or bf16 (RNE) conversion happen
 //    in the epilogue, straight from the accumulators.
+#include <algorithm>
 #include <cstdint>
 #include <type_traits>
 
@@ -445,11 +446,13 @@ __device__ __forceinline__ int chunk_swizzle(int row) { return ((row >> 1) ^ (ro
 //   accumulators hold 4 consecutive output columns of one row: the epilogue
 //   stages rows in LDS with 8-byte writes and stores 16-byte row chunks.
 // Rows past M or N read a clamped (valid) row; their outputs are never stored.
-template <int STAGES, bool kOutBf16, bool kGates, bool kSwiglu>
+// kSplit: every workgroup computes one K part of a split tail tile (see
+// SplitTail) and writes its raw fp32 sums to the workspace instead of y.
+template <int STAGES, bool kOutBf16, bool kGates, bool kSwiglu, bool kSplit = false>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const ColScales cs,
-    int M, int N, int K, void* __restrict__ y, int64_t ldy, const SwigluOut sw) {
+    int M, int N, int K, void* __restrict__ y, int64_t ldy, const SwigluOut sw, const SplitTail sp) {
   constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FM = 4, FN = 4;
   constexpr int kCodeBytes = BM * kRowBytes;          // 16 KiB per operand per stage
   constexpr int kStageScaleBytes = BM * kScaleBytes;  // 2 KiB per operand per stage
@@ -568,8 +571,18 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   };
 
 
+  // Workgroup -> tile, and the tile's K tiles [k_first, k_first + k_count):
+  // all of them, or (kSplit) part `unit % splits` of tail tile `unit / splits`.
+  int bid = blockIdx.x, k_first = 0, k_count = ksteps;
+  if constexpr (kSplit) {
+    static_assert(!kSwiglu && !kGates, "split parts carry raw sums only");
+    const int unit = blockIdx.x, piece = unit % sp.splits;
+    bid = sp.full + unit / sp.splits;
+    k_first = ksteps * piece / sp.splits;
+    k_count = ksteps * (piece + 1) / sp.splits - k_first;
+  }
   int tile_m, tile_n;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+  tile_coords(bid, tiles_m, tiles_n, tile_m, tile_n);
   const int m0 = tile_m * BM, n0 = tile_n * BN;
   set_sources(m0, n0);
   // The ring always holds STAGES copies in flight or landed.  Past the last
@@ -577,7 +590,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   // which keeps the loop body free of branches (one scheduling region, so
   // copies and LDS reads can be interleaved with the matrix instructions).
 #pragma unroll
-  for (int s = 0; s < STAGES; ++s) issue_stage(min(s, ksteps - 1), s);
+  for (int s = 0; s < STAGES; ++s) issue_stage(k_first + min(s, k_count - 1), s);
 
   floatx16_t acc[FN][FM];  // acc[j][i]: rows of W block j (output columns) x columns of A block i (output rows)
 #pragma unroll
@@ -661,9 +674,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     else lds_copy4(rws, ws_off[g - 10], kscl, st + 2 * kCodeBytes + kStageScaleBytes + (wave * 64 + 32 * (g - 10)) * kScaleBytes);
   };
 
-  for (int ks = 0; ks < ksteps; ++ks) {
-    const int slot = ks % STAGES, next_slot = (ks + 1) % STAGES;
-    const int refill = min(ks + STAGES, ksteps - 1);
+  for (int it = 0; it < k_count; ++it) {
+    const int slot = it % STAGES, next_slot = (it + 1) % STAGES;
+    const int refill = k_first + min(it + STAGES, k_count - 1);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int cur = kk & 1;
@@ -698,6 +711,21 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   }
   mfma_drain();
   wait_vmcnt<0>();  // the repeated copies past the last K tile
+  if constexpr (kSplit) {
+    // one K part of a split tile: the raw fp32 sums, thread-major in groups
+    // of 4 accumulators (group c = 16 j + 4 i + g), for the adding kernel;
+    // no LDS is touched, so no barrier
+    floatx4_t* dst = reinterpret_cast<floatx4_t*>(sp.part) + (size_t)blockIdx.x * (64 * 256) + tid;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          dst[((j * FM + i) * 4 + g) * 256] =
+              floatx4_t{acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]};
+    return;
+  }
   __syncthreads();  // every wave is done with the ring
 
   // Epilogue.  Lane (r32, half) of block (j, i) holds, for output row
@@ -905,6 +933,73 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
         // store still in flight (wrong rows in the output).
         __builtin_amdgcn_s_waitcnt(0xCF0F);  // expcnt(0); vmcnt, lgkmcnt untouched
       }
+    }
+  }
+}
+
+// Most K parts of a split tail tile.
+constexpr int kMaxSplits = 8;
+
+// Second kernel of a split tail: adds the K parts of each split tile in part
+// order (fixed, so the output is deterministic) and writes the sums as the
+// streaming kernel's epilogue does: y = sum * RN32(g_a g_w) of the column,
+// then fp32 or bf16 (RNE).  Block (t, q) covers tail tile t and the
+// accumulator groups 4q .. 4q + 3 of every thread of the workgroup that
+// computed it; thread `tid` takes the values that thread held.
+template <bool kOutBf16>
+__global__ __launch_bounds__(256) void split_tail_add_kernel(const SplitTail sp, const float* __restrict__ a_gs,
+                                                             const ColScales cs, int M, int N,
+                                                             void* __restrict__ y, int64_t ldy) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_m = wave >> 1, wave_n = wave & 1, r32 = lane & 31, half = lane >> 5;
+  const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+  const bool vec_ok = ((uintptr_t)y % 16 == 0) && (ldy % 4 == 0);
+  int tm, tn;
+  tile_coords(sp.full + (int)blockIdx.x, tiles_m, tiles_n, tm, tn);
+  // RN32(g_a g_i) of every column range, once per block
+  __shared__ float alpha_of_range[kMaxModules];
+  if (tid < cs.n) alpha_of_range[tid] = *a_gs * cs.gs[tid];
+  const floatx4_t* base = reinterpret_cast<const floatx4_t*>(sp.part) + (size_t)blockIdx.x * sp.splits * (64 * 256);
+  // every load first (up to kMaxSplits parts of 4 groups in flight), then
+  // the sums in part order
+  floatx4_t v[4][kMaxSplits];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+    for (int p = 0; p < kMaxSplits; ++p)
+      if (p < sp.splits) v[cc][p] = base[((size_t)p * 64 + 4 * blockIdx.y + cc) * 256 + tid];
+  __syncthreads();  // the alpha table is written
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    const int c = 4 * (int)blockIdx.y + cc;
+    floatx4_t sum = v[cc][0];
+#pragma unroll
+    for (int p = 1; p < kMaxSplits; ++p)
+      if (p < sp.splits) sum += v[cc][p];
+    const int j = c >> 4, i = (c >> 2) & 3, g = c & 3;
+    const int row = tm * 256 + 128 * wave_m + 32 * i + r32;
+    const int col = tn * 256 + 128 * wave_n + 32 * j + 8 * g + 4 * half;
+    if (row >= M) continue;
+    floatx4_t o;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[t] = sum[t] * alpha_of_range[col_range(cs, min(col + t, N - 1))];
+    if (vec_ok && col + 3 < N) {  // the 4 columns in one 8- or 16-byte store
+      if constexpr (kOutBf16) {
+        typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<bf4_t*>(reinterpret_cast<__bf16*>(y) + (int64_t)row * ldy + col) =
+            bf4_t{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+      } else {
+        *reinterpret_cast<floatx4_t*>(reinterpret_cast<float*>(y) + (int64_t)row * ldy + col) = o;
+      }
+      continue;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (col + t >= N) break;
+      if constexpr (kOutBf16)
+        reinterpret_cast<__bf16*>(y)[(int64_t)row * ldy + col + t] = (__bf16)o[t];
+      else
+        reinterpret_cast<float*>(y)[(int64_t)row * ldy + col + t] = o[t];
     }
   }
 }
@@ -1428,33 +1523,93 @@ bool launch_decode(const uint8_t* a_codes, const uint8_t* a_scales, const float*
   return false;
 }
 
+// Workgroups in one round of the large-tile kernel: one per CU.
+constexpr int kRound = 256;
+
+// Whether the large-tile kernel takes the shape (apart from pointer
+// alignment): K in whole 128-value steps, 32-bit buffer offsets, and at
+// least one full round of tiles.
+bool stream_shape(int64_t M, int64_t N, int64_t K) {
+  const bool fits32 = M * (K / 2) < ((int64_t)1 << 31) && N * (K / 2) < ((int64_t)1 << 31);
+  return K % kBK == 0 && fits32 && ((M + 255) / 256) * ((N + 255) / 256) >= kRound;
+}
+
+}  // namespace
+
+SplitTail gemm_split_plan(int64_t M, int64_t N, int64_t K) {
+  SplitTail sp{};
+  if (M <= 0 || N <= 0 || !stream_shape(M, N, K)) return sp;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t tail = tiles % kRound;
+  // Split only a last round at most a quarter full, into parts of at least
+  // 4 K steps, at most kMaxSplits of them (the partial sums are 256 KiB per
+  // part and are written and read once more), filling at most one round.
+  if (tail == 0 || tail > kRound / 4) return sp;
+  const int splits = (int)std::min<int64_t>(std::min<int64_t>(kRound / tail, kMaxSplits), (K / kBK) / 4);
+  if (splits < 2) return sp;
+  sp.full = (int)(tiles - tail);
+  sp.tail = (int)tail;
+  sp.splits = splits;
+  return sp;
+}
+
+size_t gemm_split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const SplitTail sp = gemm_split_plan(M, N, K);
+  return (size_t)sp.tail * (size_t)sp.splits * (64 * 256 * sizeof(floatx4_t));
+}
+
+namespace {
+
+// The large-tile launch, with the tail split when `sp.splits` > 0.
+template <bool kOutBf16, bool kGates>
+hipError_t launch_stream(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                         const uint8_t* w_codes, const uint8_t* w_scales, const ColScales& cs, int M, int N,
+                         int K, void* y, int64_t ldy, const SplitTail& sp, hipStream_t stream) {
+  constexpr int kStages = 3;
+  const int64_t tiles = ((int64_t)(M + 255) / 256) * ((N + 255) / 256);
+  // whole tiles (all of them without a split), then the K parts of the tail
+  // tiles, then their sums: three launches in stream order
+  gemm_stream_kernel<kStages, kOutBf16, kGates, false>
+      <<<dim3((unsigned)(sp.splits > 0 ? sp.full : tiles)), dim3(256), 0, stream>>>(
+          a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y, ldy, SwigluOut{}, sp);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || sp.splits == 0) return err;
+  if constexpr (!kGates) {
+    gemm_stream_kernel<kStages, false, false, false, true>
+        <<<dim3((unsigned)(sp.tail * sp.splits)), dim3(256), 0, stream>>>(
+            a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, nullptr, 0, SwigluOut{}, sp);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    split_tail_add_kernel<kOutBf16><<<dim3((unsigned)sp.tail, 16), dim3(256), 0, stream>>>(sp, a_gs, cs, M, N,
+                                                                                           y, ldy);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;  // gate epilogues are never split
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
                        const uint8_t* w_codes, const uint8_t* w_scales, const ColScales& cs,
                        int64_t M, int64_t N, int64_t K, void* y, bool out_bf16, int64_t ldy,
-                       hipStream_t stream) {
+                       hipStream_t stream, void* workspace, size_t workspace_bytes) {
   const bool aligned = (K % kBK == 0) && ((uintptr_t)a_codes % 16 == 0) && ((uintptr_t)w_codes % 16 == 0) &&
                        ((uintptr_t)a_scales % 8 == 0) && ((uintptr_t)w_scales % 8 == 0);
-  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  const bool fits32 = M * (K / 2) < ((int64_t)1 << 31) && N * (K / 2) < ((int64_t)1 << 31);
-  if (aligned && fits32 && big_tiles >= 256) {
-    constexpr int kStages = 3;
-    const dim3 grid((unsigned)big_tiles), block(256);
+  if (aligned && stream_shape(M, N, K)) {
     const bool gates = cs.decay_hi > cs.decay_lo || cs.write_hi > cs.write_lo;
-#define NVFP4_STREAM(BF16, GATES)                                                                           \
-  gemm_stream_kernel<kStages, BF16, GATES, false><<<grid, block, 0, stream>>>(a_codes, a_scales, a_gs, w_codes, \
-                                                                              w_scales, cs, (int)M, (int)N,  \
-                                                                              (int)K, y, ldy, SwigluOut{})
-    if (out_bf16) {
-      if (gates) NVFP4_STREAM(true, true);
-      else NVFP4_STREAM(true, false);
-    } else {
-      if (gates) NVFP4_STREAM(false, true);
-      else NVFP4_STREAM(false, false);
+    SplitTail sp{};
+    if (!gates && workspace && (uintptr_t)workspace % 16 == 0) {
+      sp = gemm_split_plan(M, N, K);
+      if (workspace_bytes < gemm_split_workspace_bytes(M, N, K)) sp = SplitTail{};
+      sp.part = static_cast<float*>(workspace);
     }
-#undef NVFP4_STREAM
-    return hipGetLastError();
+    const int m = (int)M, n = (int)N, k = (int)K;
+    if (out_bf16) {
+      if (gates) return launch_stream<true, true>(a_codes, a_scales, a_gs, w_codes, w_scales, cs, m, n, k, y, ldy, sp, stream);
+      return launch_stream<true, false>(a_codes, a_scales, a_gs, w_codes, w_scales, cs, m, n, k, y, ldy, sp, stream);
+    }
+    if (gates) return launch_stream<false, true>(a_codes, a_scales, a_gs, w_codes, w_scales, cs, m, n, k, y, ldy, sp, stream);
+    return launch_stream<false, false>(a_codes, a_scales, a_gs, w_codes, w_scales, cs, m, n, k, y, ldy, sp, stream);
   }
   // decode: buffer offsets of rows up to N + 63 must stay below 2^31, and
   // the scale runs of the longest K part must fit in LDS
@@ -1478,7 +1633,7 @@ hipError_t launch_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_
   cs.end[0] = (int)(2 * F);
   const int64_t tiles = ((M + 255) / 256) * ((2 * F + 255) / 256);
   gemm_stream_kernel<3, false, false, true><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(
-      a_codes, a_scales, a_gs, w_codes, w_scales, cs, (int)M, (int)(2 * F), (int)K, nullptr, 0, out);
+      a_codes, a_scales, a_gs, w_codes, w_scales, cs, (int)M, (int)(2 * F), (int)K, nullptr, 0, out, SplitTail{});
   return hipGetLastError();
 }
 

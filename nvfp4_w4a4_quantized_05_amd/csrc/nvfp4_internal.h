@@ -48,10 +48,33 @@ hipError_t launch_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_
                                        const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
                                        int64_t M, int64_t F, int64_t K, const SwigluOut& out, hipStream_t stream);
 
+// Tail split of the large-tile GEMM.  Its workgroups take 256 x 256 output
+// tiles, one per CU at a time, so a tile count just above a multiple of 256
+// leaves the last round almost empty (4096 x 12384 has 784 tiles: 3 full
+// rounds and 16 tiles).  Tiles 0 .. full - 1 are done whole; each of the
+// `tail` remaining tiles is split over K into `splits` parts whose fp32
+// partial sums go to the workspace, and a second kernel adds the parts in
+// part order and writes the output.  splits == 0: no split.
+struct SplitTail {
+  int full;
+  int tail;
+  int splits;
+  float* part;  // [tail x splits x 64 x 256 x 4] fp32 partial sums (workspace)
+};
+
+// The split for a shape on the large-tile kernel (splits == 0 when the last
+// round is more than a quarter full, or K is too short to split), and the
+// workspace bytes it needs (0 without a split).
+SplitTail gemm_split_plan(int64_t M, int64_t N, int64_t K);
+size_t gemm_split_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+// The GEMM; `workspace` (16-byte aligned, workspace_bytes) lets it split the
+// last round's tiles when gemm_split_workspace_bytes() > 0 and the
+// large-tile kernel runs without gate columns; NULL / 0 runs without.
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
                        const uint8_t* w_codes, const uint8_t* w_scales, const ColScales& cs,
                        int64_t M, int64_t N, int64_t K, void* y, bool out_bf16, int64_t ldy,
-                       hipStream_t stream);
+                       hipStream_t stream, void* workspace = nullptr, size_t workspace_bytes = 0);
 
 // Decode GEMM with the activation quantization done inside the kernel (bf16
 // X, given tensor scale).  Only for shapes where quantize_gemm_fused_fits();

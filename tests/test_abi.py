@@ -98,6 +98,52 @@ def test_gemm_rejects_bad_arguments(lib):
     assert lib.nvfp4_gemm_workspace_size(64, 12288, 5120, 0) == 0
 
 
+TILE_PART = 256 * 256 * 4  # fp32 partial sums of one 256 x 256 tile and K part
+
+
+@pytest.mark.parametrize("shape,want", [
+    # 784 tiles of 256 x 256: 3 rounds of 256 and 16 tiles, split into 8 parts
+    ((4096, 12384, 5120, 0), 16 * 8 * TILE_PART),
+    ((4096, 12384, 5120, 1), 16 * 8 * TILE_PART),          # output type does not matter
+    ((4059, 12334, 2944, 1), 16 * 5 * TILE_PART),          # 23 K steps: 5 parts of >= 4 steps
+    ((4096, 12384, 1024, 0), 16 * 2 * TILE_PART),          # 8 K steps: 2 parts
+    ((4096, 12384, 768, 0), 0),                            # 6 K steps: too short to split
+    ((4096, 12384, 5120 + 16, 0), 0),                      # K not in whole 128-value steps
+    ((4352, 4096, 5120, 0), 16 * 8 * TILE_PART),           # 272 tiles: 16 over one round
+    ((2048, 8448 + 256 * 8, 5120, 0), 0),                  # 8 x 41 = 328 tiles: last round 72 > 64
+    ((4096, 4096, 5120, 0), 0),                            # exactly one round
+    ((4096, 4096 - 256, 5120, 0), 0),                      # fewer tiles than one round
+    ((32768, 12384, 5120, 1), 0),                          # the 32K in-projection: 128-tile last round
+    ((32768, 34816, 5120, 1), 0), ((32768, 5120, 17408, 1), 0), ((32768, 5120, 4096, 1), 0),
+])
+def test_gemm_workspace_size_is_the_tail_split(lib, shape, want):
+    """nvfp4_gemm_workspace_size: the fp32 partial sums of the split tail
+    tiles (tail tiles x parts x 256 KiB), 0 for shapes without a split."""
+    assert lib.nvfp4_gemm_workspace_size(*shape) == want
+
+
+def test_gemm_tail_split_needs_its_workspace(lib):
+    """A shape with a tail split: too little workspace, a NULL or misaligned
+    workspace are refused before any HIP call; the gated epilogue (which never
+    splits) takes none."""
+    M, N, K = 4096, 12384, 5120
+    need = lib.nvfp4_gemm_workspace_size(M, N, K, 0)
+    assert need > 0
+    p = [P16] * 6
+    assert lib.nvfp4_gemm(*p, M, N, K, P16, 0, N, None, need - 1, None) == WORKSPACE
+    assert lib.nvfp4_gemm(*p, M, N, K, P16, 0, N, None, 0, None) == WORKSPACE
+    assert lib.nvfp4_gemm(*p, M, N, K, P16, 0, N, None, need, None) == NULL
+    assert lib.nvfp4_gemm(*p, M, N, K, P16, 0, N, ctypes.c_void_p(0x10008), need, None) == ALIGN
+    rows = (ctypes.c_int64 * 1)(N)
+    assert lib.nvfp4_gemm_segmented(*[P16] * 5, P16, rows, 1, M, K, P16, 0, N, None, 0, None) == WORKSPACE
+    # gates: no workspace needed, so the call gets past the workspace check
+    # to the gate-parameter check (a NULL a_log)
+    rows3 = (ctypes.c_int64 * 3)(12288, 48, 48)
+    assert lib.nvfp4_gemm_segmented_gates(*[P16] * 5, P16, rows3, 3, 1, None, P16, 2, M, K, P16, 0, N,
+                                          None, 0, None) == NULL
+    assert lib.nvfp4_last_hip_error() == 0
+
+
 def gs_(lib, rows=(8, 0, 4), M=4, K=32, y=P16, od=0, ldy=12, ptrs=None, mgs=P16, n=None, host_rows=True):
     p = ptrs or [P16] * 5
     arr = (ctypes.c_int64 * max(len(rows), 1))(*rows) if host_rows else None
