@@ -191,8 +191,8 @@ NVFP4_API nvfp4_status_t nvfp4_gemm_segmented(const uint8_t* a_codes, const uint
  *                  may be NULL when decay_module is -1
  *   write_module   index of the write-strength module (the b projection),
  *                  or -1; different from decay_module unless both are -1
- * The gated epilogue never splits tiles, so this call needs no workspace
- * (workspace may be NULL and workspace_bytes 0).
+ * It splits the same tail tiles as nvfp4_gemm_segmented (the K parts are
+ * added first, then the gates applied), so it takes the same workspace.
  * NVFP4_ERR_SHAPE for a module index outside -1 .. n_modules - 1 or equal
  * indices; NVFP4_ERR_NULL / NVFP4_ERR_ALIGN (4 bytes) for the gate
  * parameters; other errors as for nvfp4_gemm_segmented.  Accuracy: the
@@ -401,7 +401,8 @@ NVFP4_API nvfp4_status_t nvfp4_harmonize_fused_scales(uint8_t* scales, const flo
                                             int64_t K, float* shared_gs, uint32_t* counters,
                                             void* stream);
 
-/* Bytes of workspace nvfp4_gemm and nvfp4_gemm_segmented need for this
+/* Bytes of workspace nvfp4_gemm, nvfp4_gemm_segmented and
+ * nvfp4_gemm_segmented_gates need for this
  * shape: the partial sums of the split tail tiles (256 KiB per tile and
  * part), 0 for every shape without a tail split (out_dtype does not change
  * it).  4096 x 12384 x 5120 needs 32 MiB; the 32K-token projections, the

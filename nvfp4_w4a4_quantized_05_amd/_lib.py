@@ -250,7 +250,8 @@ def gemm_segmented_gates(a_codes, a_scales, a_gs, w_codes, w_scales, module_gs, 
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
     lib = load()
-    ws, ws_bytes = None, 0  # the gated epilogue takes no workspace
+    ws_bytes = lib.nvfp4_gemm_workspace_size(M, N, K, od)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a_codes.device) if ws_bytes else None
     host_rows = (ctypes.c_int64 * len(rows))(*rows)
     st = lib.nvfp4_gemm_segmented_gates(_ptr(a_codes), _ptr(a_scales), _ptr(a_gs), _ptr(w_codes), _ptr(w_scales),
                                         _ptr(module_gs.contiguous()), host_rows, len(rows), decay_module,

@@ -25,8 +25,12 @@ ARCH = "gfx950"
 # Packed fp32 ops are disabled on purpose: the compiler must not form
 # v_pk_{add,mul,fma}_f32 from scalar float code (the host pass warns that it
 # does not know the feature; that warning is harmless).
+# The unroll threshold lets the 16x16x32 streaming kernel unroll its 256
+# matrix instructions per K step fully (register arrays indexed by constants);
+# every other kernel compiles to the same code with or without it.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-pragma-unroll-threshold=1000000",
           "-I", os.path.join(ROOT, "include"), "-fvisibility=hidden", "-Wall", "-Wno-unused-function"]
 
 

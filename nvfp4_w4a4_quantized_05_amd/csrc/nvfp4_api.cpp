@@ -36,9 +36,7 @@ nvfp4_status_t gemm_checked(const uint8_t* a_codes, const uint8_t* a_scales, con
     return NVFP4_ERR_ALIGN;
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   if (tiles > (int64_t)INT_MAX) return NVFP4_ERR_SHAPE;
-  // the gate epilogue never splits tiles, so it takes no workspace
-  const bool gates = cs.decay_hi > cs.decay_lo || cs.write_hi > cs.write_lo;
-  const size_t need = gates ? 0 : nvfp4::gemm_split_workspace_bytes(M, N, K);
+  const size_t need = nvfp4::gemm_split_workspace_bytes(M, N, K);
   if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
   if (need > 0 && !workspace) return NVFP4_ERR_NULL;
   if (need > 0 && !aligned(workspace, 16)) return NVFP4_ERR_ALIGN;

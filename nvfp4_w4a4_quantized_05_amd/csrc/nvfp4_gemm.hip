@@ -431,10 +431,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // 16-lane phase of ds_read_b128.
 __device__ __forceinline__ int chunk_swizzle(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-// Streaming kernel for the large shapes (K % 128 == 0, aligned operands).
+// Gate/up GEMM with SwiGLU and NVFP4 quantization in its epilogue
+// (K % 128 == 0, aligned operands; the weight rows are [gate; up]).  Its
+// main loop is the earlier large-tile design on 32x32x16 matrix
+// instructions; the plain and gated GEMMs moved to gemm_stream16_kernel.
 //
-// * 256 x 256 output tile per workgroup, 4 waves of 128 x 128 (4 x 4 blocks
-//   of 32 x 32), accumulators in AGPRs.
+// * 256 x 256 output tile per workgroup (128 output columns: their gate and
+//   up rows), 4 waves of 128 x 128 (4 x 4 blocks of 32 x 32), accumulators
+//   in AGPRs.
 // * K tiles of 128 values stream through a STAGES-deep LDS ring filled by
 //   direct global -> LDS copies (no VGPR staging), STAGES K tiles ahead.
 // * Each K tile is consumed in two halves.  While the MFMAs of one half run,
@@ -443,31 +447,20 @@ __device__ __forceinline__ int chunk_swizzle(int row) { return ((row >> 1) ^ (ro
 //   refilled and the next K tile's first half read.  No wait on LDS or on
 //   memory is then exposed in steady state except the barrier itself.
 // * The MFMA takes W as its "A" operand and A as "B", so each lane's
-//   accumulators hold 4 consecutive output columns of one row: the epilogue
-//   stages rows in LDS with 8-byte writes and stores 16-byte row chunks.
-// Rows past M or N read a clamped (valid) row; their outputs are never stored.
-// kSplit: every workgroup computes one K part of a split tail tile (see
-// SplitTail) and writes its raw fp32 sums to the workspace instead of y.
-template <int STAGES, bool kOutBf16, bool kGates, bool kSwiglu, bool kSplit = false>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(
+//   accumulators hold 4 consecutive output columns of one row.
+// Rows past M or F read a clamped (valid) row; their outputs are never stored.
+template <int STAGES>
+__global__ __launch_bounds__(256) void gemm_swiglu_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const ColScales cs,
-    int M, int N, int K, void* __restrict__ y, int64_t ldy, const SwigluOut sw, const SplitTail sp) {
+    int M, int N, int K, const SwigluOut sw) {
   constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FM = 4, FN = 4;
   constexpr int kCodeBytes = BM * kRowBytes;          // 16 KiB per operand per stage
   constexpr int kStageScaleBytes = BM * kScaleBytes;  // 2 KiB per operand per stage
   constexpr int kStageBytes = 2 * kCodeBytes + 2 * kStageScaleBytes;
   constexpr int kLoadsPerStage = 12;                  // vector-memory instructions per wave per stage
-  using out_t = typename std::conditional<kOutBf16, __bf16, float>::type;
-  constexpr int kEsz = sizeof(out_t);
-  // Output staged per pass: a whole 32-row block (every lane then writes in
-  // every pass) by 256 bytes of each row: all 128 columns of the wave for
-  // bf16, half of them for fp32.
-  constexpr int kStripRows = 32;
-  constexpr int kColPasses = kOutBf16 ? 1 : 2;
-  constexpr int kStripCols = WN / kColPasses;
-  constexpr int kStripRow = kStripCols * kEsz + 16;   // staged row bytes (+16 against bank conflicts)
-  constexpr int kStripBytes = kStripRows * kStripRow;
+  // per-wave fp32 staging of h, 32 rows x 64 columns (rows padded by 16 bytes)
+  constexpr int kStripBytes = 32 * (64 * 4 + 16);
   static_assert(STAGES >= 3, "ring depth");
   static_assert((STAGES - 1) * kLoadsPerStage < 64, "vmcnt range");
   constexpr int kAlphaBytes = WN * 4;                 // per-wave column scale table
@@ -482,7 +475,6 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int64_t row_bytes = K / 2, srow_bytes = K / 16;
   const int ksteps = K / kBK;
-  const bool vec_ok = ((uintptr_t)y % 16 == 0) && ((ldy * kEsz) % 16 == 0);
 
   // Per-lane copy offsets of the current tile (32-bit, within buffer
   // resources whose size bounds every read).  Wave w copies rows
@@ -494,20 +486,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_scales, (int64_t)M * srow_bytes);
   const __amdgpu_buffer_rsrc_t rws = make_rsrc(w_scales, (int64_t)N * srow_bytes);
   uint32_t a_off[4], w_off[4], as_off[2], ws_off[2];
-  // W row of tile row r.  kSwiglu: the tile's 256 rows are gate and up rows
-  // of its 128 output columns c0 = n0 / 2 .. + 127, in blocks of 32: wave
-  // half wn = r / 128 covers columns c0 + 64 wn + 32 b + e (b = (r / 64) % 2,
-  // e = r % 32), rows 32 b .. of the half being gate (r / 32 even) or up
-  // (odd).  So a lane's accumulator blocks j = 0, 2 (gate) and 1, 3 (up) hold
-  // the same output elements.  Rows past F repeat row F - 1 (outputs past F
-  // are not written).
+  // W row of tile row r: the tile's 256 rows are gate and up rows of its 128
+  // output columns c0 = n0 / 2 .. + 127, in blocks of 32: wave half wn =
+  // r / 128 covers columns c0 + 64 wn + 32 b + e (b = (r / 64) % 2, e = r %
+  // 32), rows 32 b .. of the half being gate (r / 32 even) or up (odd).  So
+  // a lane's accumulator blocks j = 0, 2 (gate) and 1, 3 (up) hold the same
+  // output elements.  Rows past F repeat row F - 1 (outputs past F are not
+  // written).
   auto w_row = [&](int n0, int r) -> int {
-    if constexpr (kSwiglu) {
-      const int col = n0 / 2 + 64 * (r >> 7) + 32 * ((r >> 6) & 1) + (r & 31);
-      return min(col, sw.F - 1) + (((r >> 5) & 1) ? sw.F : 0);
-    } else {
-      return min(n0 + r, N - 1);
-    }
+    const int col = n0 / 2 + 64 * (r >> 7) + 32 * ((r >> 6) & 1) + (r & 31);
+    return min(col, sw.F - 1) + (((r >> 5) & 1) ? sw.F : 0);
   };
   auto set_sources = [&](int m0, int n0) {
 #pragma unroll
@@ -571,18 +559,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   };
 
 
-  // Workgroup -> tile, and the tile's K tiles [k_first, k_first + k_count):
-  // all of them, or (kSplit) part `unit % splits` of tail tile `unit / splits`.
-  int bid = blockIdx.x, k_first = 0, k_count = ksteps;
-  if constexpr (kSplit) {
-    static_assert(!kSwiglu && !kGates, "split parts carry raw sums only");
-    const int unit = blockIdx.x, piece = unit % sp.splits;
-    bid = sp.full + unit / sp.splits;
-    k_first = ksteps * piece / sp.splits;
-    k_count = ksteps * (piece + 1) / sp.splits - k_first;
-  }
   int tile_m, tile_n;
-  tile_coords(bid, tiles_m, tiles_n, tile_m, tile_n);
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
   const int m0 = tile_m * BM, n0 = tile_n * BN;
   set_sources(m0, n0);
   // The ring always holds STAGES copies in flight or landed.  Past the last
@@ -590,7 +568,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   // which keeps the loop body free of branches (one scheduling region, so
   // copies and LDS reads can be interleaved with the matrix instructions).
 #pragma unroll
-  for (int s = 0; s < STAGES; ++s) issue_stage(k_first + min(s, k_count - 1), s);
+  for (int s = 0; s < STAGES; ++s) issue_stage(min(s, ksteps - 1), s);
 
   floatx16_t acc[FN][FM];  // acc[j][i]: rows of W block j (output columns) x columns of A block i (output rows)
 #pragma unroll
@@ -674,9 +652,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     else lds_copy4(rws, ws_off[g - 10], kscl, st + 2 * kCodeBytes + kStageScaleBytes + (wave * 64 + 32 * (g - 10)) * kScaleBytes);
   };
 
-  for (int it = 0; it < k_count; ++it) {
-    const int slot = it % STAGES, next_slot = (it + 1) % STAGES;
-    const int refill = k_first + min(it + STAGES, k_count - 1);
+  for (int ks = 0; ks < ksteps; ++ks) {
+    const int slot = ks % STAGES, next_slot = (ks + 1) % STAGES;
+    const int refill = min(ks + STAGES, ksteps - 1);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int cur = kk & 1;
@@ -711,90 +689,394 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   }
   mfma_drain();
   wait_vmcnt<0>();  // the repeated copies past the last K tile
+  __syncthreads();  // every wave is done with the ring
+
+  const float g_a = *a_gs;
+  // h = silu(g) u of the wave's 64 output columns c_out .. + 63 (v = acc
+  // RN32(g_a g_w) for both), staged in fp32 in the wave's strip buffer, 32
+  // rows at a time: 32 x 64 values, i.e. 128 blocks of 16, two per lane.
+  // Each lane then quantizes its blocks with the quantize kernel's
+  // arithmetic and stores 8 code bytes and 1 scale byte per block (and, if
+  // asked, the 16 fp32 values).
+  static_assert(kStripBytes >= 32 * 64 * 4, "fp32 strip of 32 x 64");
+  const float alpha = g_a * cs.gs[0];
+  const int c_out = n0 / 2 + 64 * wave_n;
+  float* fs = reinterpret_cast<float*>(smem + STAGES * kStageBytes + wave * kStripBytes);
+  const float hg = *sw.gs, r6 = __builtin_amdgcn_rcpf(6.0f * hg);
+  const int qr = lane >> 2, qb = lane & 3;  // the lane's blocks: rows qr and 16 + qr, 16-column block qb
+  if (c_out < sw.F) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      // the 32 rows of block i, every lane writing its values
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float gv = acc[2 * jj][i][v] * alpha, uv = acc[2 * jj + 1][i][v] * alpha;
+          fs[r32 * 64 + 32 * jj + (v >> 2) * 8 + half * 4 + (v & 3)] = silu_fast(gv) * uv;
+        }
+      __asm__ volatile("" ::: "memory");  // other lanes' values are read below
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int row = m0 + wave_m * WM + i * 32 + sub * 16 + qr;
+        const floatx4_t* src = reinterpret_cast<const floatx4_t*>(fs + (sub * 16 + qr) * 64 + 16 * qb);
+        float vals[16];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const floatx4_t f4 = src[e];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) vals[4 * e + t] = f4[t];
+        }
+        if (row < M) {
+          uint32_t w0, w1;
+          const uint32_t sc = quantize_block(vals, hg, r6, w0, w1);
+          const int col = c_out + 16 * qb;
+          *reinterpret_cast<u32x2_t*>(sw.codes + (int64_t)row * (sw.F / 2) + col / 2) = u32x2_t{w0, w1};
+          sw.scales[(int64_t)row * (sw.F / 16) + col / 16] = (uint8_t)sc;
+          if (sw.h) {
+            floatx4_t* dst = reinterpret_cast<floatx4_t*>(sw.h + (int64_t)row * sw.ldh + col);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[e] = floatx4_t{vals[4 * e], vals[4 * e + 1], vals[4 * e + 2], vals[4 * e + 3]};
+          }
+        }
+      }
+      // the stores above must have read their data registers before the
+      // next block's LDS reads may land in them (a later ds_read into the
+      // registers of a store still in flight was seen to overwrite its data)
+      __builtin_amdgcn_s_waitcnt(0xCF0F);  // expcnt(0); vmcnt, lgkmcnt untouched
+      __asm__ volatile("" ::: "memory");  // reads done before the next block is written
+    }
+  }
+}
+
+// v_mfma_f32_16x16x32_f16 with the accumulator pinned in AGPRs (dst = srcC).
+// Written as inline asm because the compiler, given 64 such accumulators
+// through the builtin, shuttled them between AGPRs and VGPRs on every pass
+// of the loop (256 copies each way per 256 matrix instructions).  The
+// compiler does not track hazards into inline asm, so the kernel keeps its
+// own distances: no accumulator is read by the next 63 matrix instructions,
+// every operand is written at least 8 matrix instructions before its reader
+// and at least 8 after its last reader, the accumulators are zeroed long
+// before the first one, and mfma16_drain() runs before any other use.
+__device__ __forceinline__ void mfma16(floatx4_t& acc, const half8_t& a, const half8_t& b) {
+  __asm__ volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// 24 wait states after the last matrix instruction, before its results (or
+// its operand registers) are touched by anything else.
+__device__ __forceinline__ void mfma16_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Streaming kernel for the large shapes (K % 128 == 0, aligned operands) on
+// 16x16x32 matrix instructions: the plain epilogue (every output column
+// times its range's RN32(g_a g_w)), with kGates the GDN gate functions on
+// the gate columns, and with kSplit the K parts of a split tail.
+//
+//  * 256 x 256 output tile per workgroup, 4 waves of 128 x 128 (8 x 8 blocks
+//    of 16 x 16), accumulators in AGPRs; tile order as tile_coords().
+//  * K steps of 128 values stream through a 3-deep LDS ring filled by direct
+//    global -> LDS copies (no VGPR staging), 3 K steps ahead; 16-byte code
+//    chunks of each row XOR-swizzled by chunk_swizzle(row).
+//
+// Why 16x16x32: with operands of dequantized NVFP4 values that change every
+// instruction, all CUs busy and the dequantization's VALU work interleaved
+// at this kernel's ratio, v_mfma_f32_16x16x32_f16 sustained 1,990 TFLOP/s on
+// an MI355X against 1,619 for v_mfma_f32_32x32x16_f16 (register-only probe,
+// same box, back to back): the board holds its power limit under this load,
+// and the 16x16 form moves fewer accumulator bytes per multiply-add.
+//
+//  * Operand layout: lane (r16 = L % 16, q = L / 16) supplies 8 K values of
+//    row r16 of a 16-row block, for W (the instruction's A operand) and A
+//    alike; its accumulators hold output columns 4q .. 4q + 3 of the W block
+//    for output row r16 of the A block.
+//  * K mapping: a stage of 128 K values is used in 4 steps of 32.  Lane
+//    group q owns the 32 values of 16-byte chunk q of each row (scale blocks
+//    2q, 2q + 1) and reads them 8 bytes at a time: pair u (steps 2u, 2u + 1)
+//    is the chunk's half h = (u + q) & 1, so the 64 lanes of one 8-byte read
+//    hit distinct LDS banks (rows 4 apart share banks; the chunk swizzle
+//    separates them, the rotation by q the lane groups).  At step t a lane
+//    uses dword t & 1 of its pair, the same K values for both operands.
+//  * Registers: pair 0 and pair 1 of the codes (64 VGPRs); A operands
+//    double-buffered by step (64), dequantized one step ahead; W operands in
+//    4 rotating buffers, block j + 1 dequantized during block j's MFMAs.  A
+//    VALU write into an operand register therefore comes at least 12 MFMAs
+//    after the register's last MFMA read.
+//  * Per stage: the next stage's pair 0 and scale bytes are read after the
+//    mid-tile barrier (step 2), pair 1 of the current stage during step 0.
+template <int STAGES, bool kOutBf16, bool kGates, bool kSplit>
+__global__ __launch_bounds__(256) void gemm_stream16_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
+    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const ColScales cs,
+    int M, int N, int K, void* __restrict__ y, int64_t ldy, const SplitTail sp) {
+  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FB = 8;  // 16-row blocks per operand per wave
+  constexpr int kCodeBytes = BM * kRowBytes;          // 16 KiB per operand per stage
+  constexpr int kStageScaleBytes = BM * kScaleBytes;  // 2 KiB per operand per stage
+  constexpr int kStageBytes = 2 * kCodeBytes + 2 * kStageScaleBytes;
+  constexpr int kLoadsPerStage = 12;
+  using out_t = typename std::conditional<kOutBf16, __bf16, float>::type;
+  constexpr int kEsz = sizeof(out_t);
+  constexpr int kStripRows = 32;
+  constexpr int kColPasses = kOutBf16 ? 1 : 2;
+  constexpr int kStripCols = WN / kColPasses;
+  constexpr int kStripRow = kStripCols * kEsz + 16;
+  constexpr int kStripBytes = kStripRows * kStripRow;
+  static_assert(STAGES >= 3, "ring depth");
+  static_assert((STAGES - 1) * kLoadsPerStage < 64, "vmcnt range");
+  constexpr int kAlphaBytes = WN * 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStageBytes + 4 * kStripBytes + 4 * kAlphaBytes];
+  uint8_t* const ring = smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_m = wave >> 1, wave_n = wave & 1;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int64_t row_bytes = K / 2, srow_bytes = K / 16;
+  const int ksteps = K / kBK;
+  const bool vec_ok = ((uintptr_t)y % 16 == 0) && ((ldy * kEsz) % 16 == 0);
+
+  // Copies: wave w copies rows 64w .. 64w + 63 of both operands (codes with
+  // 4 instructions of 16 rows x 4 swizzled 16-byte chunks, scales with 2 of
+  // 32 rows x 2 dwords); rows past an operand are clamped to its last row.
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_codes, (int64_t)M * row_bytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_codes, (int64_t)N * row_bytes);
+  const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_scales, (int64_t)M * srow_bytes);
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(w_scales, (int64_t)N * srow_bytes);
+  uint32_t a_off[4], w_off[4], as_off[2], ws_off[2];
+  auto set_sources = [&](int m0, int n0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wave * 64 + 16 * i + (lane >> 2);
+      const int chunk = (lane & 3) ^ chunk_swizzle(row);
+      a_off[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)row_bytes + chunk * 16;
+      w_off[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)row_bytes + chunk * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = wave * 64 + 32 * i + (lane >> 1);
+      as_off[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)srow_bytes + (lane & 1) * 4;
+      ws_off[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)srow_bytes + (lane & 1) * 4;
+    }
+  };
+  auto issue_one = [&](int ks, int slot, int g) {
+    uint8_t* st = ring + slot * kStageBytes;
+    const uint32_t kc = (uint32_t)ks * kRowBytes, kscl = (uint32_t)ks * kScaleBytes;
+    if (g < 4) lds_copy16(ra, a_off[g], kc, st + (wave * 64 + 16 * g) * kRowBytes);
+    else if (g < 8) lds_copy16(rw, w_off[g - 4], kc, st + kCodeBytes + (wave * 64 + 16 * (g - 4)) * kRowBytes);
+    else if (g < 10) lds_copy4(ras, as_off[g - 8], kscl, st + 2 * kCodeBytes + (wave * 64 + 32 * (g - 8)) * kScaleBytes);
+    else lds_copy4(rws, ws_off[g - 10], kscl, st + 2 * kCodeBytes + kStageScaleBytes + (wave * 64 + 32 * (g - 10)) * kScaleBytes);
+  };
+
+  // Accumulators, zeroed in AGPRs long before the first matrix instruction
+  // reads them (the instructions are inline asm, which the compiler's hazard
+  // tracking does not see into).
+  floatx4_t acc[FB][FB];  // acc[j][i]: W block j (output columns) x A block i (output rows)
+#pragma unroll
+  for (int j = 0; j < FB; ++j)
+#pragma unroll
+    for (int i = 0; i < FB; ++i) {
+      acc[j][i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      __asm__ volatile("" : "+a"(acc[j][i]));
+    }
+
+  // Workgroup -> tile, and the tile's K steps [k_first, k_first + k_count):
+  // all of them, or (kSplit) part `unit % splits` of tail tile `unit / splits`.
+  int bid = blockIdx.x, k_first = 0, k_count = ksteps;
   if constexpr (kSplit) {
-    // one K part of a split tile: the raw fp32 sums, thread-major in groups
-    // of 4 accumulators (group c = 16 j + 4 i + g), for the adding kernel;
-    // no LDS is touched, so no barrier
-    floatx4_t* dst = reinterpret_cast<floatx4_t*>(sp.part) + (size_t)blockIdx.x * (64 * 256) + tid;
+    const int unit = blockIdx.x, piece = unit % sp.splits;
+    bid = sp.full + unit / sp.splits;
+    k_first = ksteps * piece / sp.splits;
+    k_count = ksteps * (piece + 1) / sp.splits - k_first;
+  }
+  int tile_m, tile_n;
+  tile_coords(bid, tiles_m, tiles_n, tile_m, tile_n);
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+  set_sources(m0, n0);
+  // The ring always holds STAGES copies in flight or landed; past the last
+  // K step the copies repeat it into a slot nobody reads again.
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+  for (int s = 0; s < STAGES; ++s)
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int g = 0; g < kLoadsPerStage; ++g) issue_one(k_first + min(s, k_count - 1), s, g);
+
+  // Per-lane LDS offsets within a stage.  Row R = 128 w + 16 b + r16 of an
+  // operand: chunk q sits at chunk position q ^ chunk_swizzle(R), and
+  // chunk_swizzle(R) = chunk_swizzle(r16) ^ 2 (b & 1).
+  const int s0 = chunk_swizzle(r16);
+  uint32_t lo[2][2];  // [block parity][pair]
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          dst[((j * FM + i) * 4 + g) * 256] =
-              floatx4_t{acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]};
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) lo[p][u] = r16 * kRowBytes + 16 * (q ^ s0 ^ (2 * p)) + 8 * ((u + q) & 1);
+  const uint32_t lsc = r16 * kScaleBytes + 2 * q;  // the lane's scale bytes 2q, 2q + 1 of its row
+  // v_perm selector packing the scale bytes of blocks 2k, 2k + 1 into one
+  // dword, swapped for odd q so that pair u's byte is byte u (block 2k) and
+  // byte 2 + u (block 2k + 1)
+  const uint32_t psel = (q & 1) ? 0x04050001u : 0x05040100u;
+
+  u32x2_t ra2[2][FB], rw2[2][FB];  // code pairs u = 0, 1 of the lane's rows
+  uint32_t asc[4], wsc[4], asc_n[4], wsc_n[4], xs[2 * FB];
+  half8_t af[2][FB], wf[4];
+  half2_t ta[4], tw[4];
+  uint32_t spa = 0, spw = 0;
+
+  auto read_pair = [&](uint32_t stage, int u, int g) {  // g < 8: A block g, else W block g - 8
+    const int b = g & 7;
+    if (g < FB)
+      ra2[u][b] = *reinterpret_cast<const u32x2_t*>(ring + stage + wave_m * WM * kRowBytes + 16 * kRowBytes * b + lo[b & 1][u]);
+    else
+      rw2[u][b] = *reinterpret_cast<const u32x2_t*>(ring + stage + kCodeBytes + wave_n * WN * kRowBytes +
+                                                    16 * kRowBytes * b + lo[b & 1][u]);
+  };
+  auto read_scale = [&](uint32_t stage, int g) {
+    const int b = g & 7;
+    const uint32_t base = g < FB ? 2 * kCodeBytes + wave_m * WM * kScaleBytes
+                                 : 2 * kCodeBytes + kStageScaleBytes + wave_n * WN * kScaleBytes;
+    xs[g] = *reinterpret_cast<const uint16_t*>(ring + stage + base + 16 * kScaleBytes * b + lsc);
+  };
+  auto pack_scales = [&](uint32_t (&as)[4], uint32_t (&ws)[4], int k) {  // k = 0..7
+    if (k < 4) as[k] = __builtin_amdgcn_perm(xs[2 * k + 1], xs[2 * k], psel);
+    else ws[k - 4] = __builtin_amdgcn_perm(xs[2 * (k - 4) + 9], xs[2 * (k - 4) + 8], psel);
+  };
+  // scale pair (fp16 bits) of block b at pair u
+  auto sbyte = [&](const uint32_t (&sc)[4], int b, int u) -> uint32_t {
+    return scale_pair((sc[b >> 1] >> (8 * (2 * (b & 1) + u))) & 0xFFu);
+  };
+  auto cvt = [&](uint32_t codes, int k) -> half2_t {
+    if (k == 0) return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0);
+    if (k == 1) return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1);
+    if (k == 2) return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2);
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3);
+  };
+  // piece k (0..7) of dequantizing 8 codes into dst: 4 conversions, then 4
+  // multiplies by the scale pair (taken at piece 1)
+  auto piece = [&](half2_t (&tmp)[4], uint32_t& s2, uint32_t codes, uint32_t scale2, half8_t& dst, int k) {
+    if (k == 1) s2 = scale2;
+    if (k < 4) {
+      tmp[k] = cvt(codes, k);
+    } else {
+      const half2_t v = tmp[k - 4] * __builtin_bit_cast(half2_t, s2);
+      dst[2 * (k - 4)] = v[0];
+      dst[2 * (k - 4) + 1] = v[1];
+    }
+  };
+
+  // first K step: wait for its copies, read its pair 0 and scales, and
+  // dequantize step 0 of A and block 0 of W
+  wait_vmcnt<(STAGES - 1) * kLoadsPerStage>();
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int g = 0; g < 2 * FB; ++g) read_pair(0, 0, g);
+#pragma unroll
+  for (int g = 0; g < 2 * FB; ++g) read_scale(0, g);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) pack_scales(asc, wsc, k);
+#pragma unroll
+  for (int b = 0; b < FB; ++b)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) piece(ta, spa, ra2[0][b][0], sbyte(asc, b, 0), af[0][b], k);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) piece(tw, spw, rw2[0][0][0], sbyte(wsc, 0, 0), wf[0], k);
+  // block 1: converted here, multiplied in the first slots of the loop
+#pragma unroll
+  for (int k = 0; k < 4; ++k) piece(tw, spw, rw2[0][1][0], sbyte(wsc, 1, 0), wf[1], k);
+  // the first operands are in their registers, and 8 wait states pass,
+  // before the first matrix instruction
+  keep_live(af[0], wf);
+  __asm__ volatile("s_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // One K step of 128 values in ring slot `slot` (a compile-time constant,
+  // so every LDS address is a loop-invariant register plus an immediate).
+  auto run_stage = [&](int it, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value, next_slot = (slot + 1) % STAGES;
+    constexpr uint32_t cur = (uint32_t)slot * kStageBytes, nxt = (uint32_t)next_slot * kStageBytes;
+    const int refill = k_first + min(it + STAGES, k_count - 1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t == 2) {
+        // mid-stage: the next stage has landed (own copies + barrier) and
+        // every wave has read this slot (pair 1 in step 0), so the slot is
+        // refilled; a bare s_barrier keeps the other copies in flight
+        wait_vmcnt<(STAGES - 2) * kLoadsPerStage>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int n = 0; n < FB * FB; ++n) {
+        const int j = n >> 3, i = n & 7;
+        mfma16(acc[j][i], wf[j & 3], af[t & 1][i]);
+        // A block j of the next step (the next stage's step 0 at t == 3)
+        if (t < 3)
+          piece(ta, spa, ra2[(t + 1) >> 1][j][(t + 1) & 1], sbyte(asc, j, (t + 1) >> 1), af[(t + 1) & 1][j], i);
+        else
+          piece(ta, spa, ra2[0][j][0], sbyte(asc_n, j, 0), af[0][j], i);
+        // W, 4 slots behind A so that no slot holds both scale extractions:
+        // slots 4-7 of block j convert block j + 2, slots 0-3 multiply block
+        // j + 1 (converted in block j - 1); blocks past 7 are the next
+        // step's (the next stage's at t == 3)
+        {
+          const int jb = i < 4 ? j + 1 : j + 2, kw = i < 4 ? i + 4 : i - 4;
+          if (jb < 8)
+            piece(tw, spw, rw2[t >> 1][jb][t & 1], sbyte(wsc, jb, t >> 1), wf[jb & 3], kw);
+          else if (t < 3)
+            piece(tw, spw, rw2[(t + 1) >> 1][jb - 8][(t + 1) & 1], sbyte(wsc, jb - 8, (t + 1) >> 1), wf[jb & 3], kw);
+          else
+            piece(tw, spw, rw2[0][jb - 8][0], sbyte(wsc_n, jb - 8, 0), wf[jb & 3], kw);
+        }
+        if (t == 0 && n < 2 * FB) read_pair(cur, 1, n);  // pair 1 of this stage
+        if (t == 2 && n < kLoadsPerStage) issue_one(refill, slot, n);
+        if (t == 2 && n >= 12 && n < 12 + 2 * FB) read_pair(nxt, 0, n - 12);  // the next stage's pair 0
+        if (t == 2 && n >= 28 && n < 28 + 2 * FB) read_scale(nxt, n - 28);    // and its scales
+        if (t == 2 && n >= 48 && (n & 1) == 0) pack_scales(asc_n, wsc_n, (n - 48) >> 1);  // not in scale slots
+        // the operands of the matrix instruction 4 slots back stay allocated
+        // until here, so no new value lands in their registers right behind
+        // their last read (the previous step's at n < 4)
+        if (n >= 4) {
+          __asm__ volatile("" ::"v"(wf[((n - 4) >> 3) & 3]), "v"(af[t & 1][(n - 4) & 7]));
+        } else {
+          __asm__ volatile("" ::"v"(wf[3]), "v"(af[(t + 1) & 1][4 + n]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      asc[k] = asc_n[k];
+      wsc[k] = wsc_n[k];
+    }
+  };
+  static_assert(STAGES == 3, "the stage loop is unrolled by the ring depth");
+  for (int it = 0; it < k_count; it += STAGES) {
+    run_stage(it, std::integral_constant<int, 0>{});
+    if (it + 1 < k_count) run_stage(it + 1, std::integral_constant<int, 1>{});
+    if (it + 2 < k_count) run_stage(it + 2, std::integral_constant<int, 2>{});
+  }
+  mfma16_drain();
+  wait_vmcnt<0>();  // the repeated copies past the last K step
+
+  if constexpr (kSplit) {
+    // one K part of a split tile: its raw fp32 sums, row-major [256 x 256],
+    // for the adding kernel; no LDS is touched, so no barrier
+    float* dst = sp.part + (size_t)blockIdx.x * (256 * 256);
+#pragma unroll
+    for (int j = 0; j < FB; ++j)
+#pragma unroll
+      for (int i = 0; i < FB; ++i) {
+        const int row = wave_m * WM + 16 * i + r16, col = wave_n * WN + 16 * j + 4 * q;
+        *reinterpret_cast<floatx4_t*>(dst + row * 256 + col) = acc[j][i];
+      }
     return;
   }
   __syncthreads();  // every wave is done with the ring
 
-  // Epilogue.  Lane (r32, half) of block (j, i) holds, for output row
-  // m = m0 + 128 wave_m + 32 i + r32, the columns n0 + 128 wave_n + 32 j +
-  // 8 (v / 4) + 4 half + (v % 4), v = 0..15: four consecutive columns per
-  // group of 4 accumulators.  Rows go through LDS in strips of 32 rows by
-  // 256 bytes (128 bf16 or 64 fp32 columns).  RN32(g_a g_w) of the wave's 128 columns goes to a
-  // small LDS table, from which each lane reads the scales of its 64
-  // columns once.  When one column range covers all 128 columns (every plain
-  // GEMM, and most tiles of a segmented one) the table is filled with one
-  // value, found with one lookup.
+  // Epilogue.  Lane (r16, q) of block
+  // (j, i) holds row m0 + 128 wave_m + 16 i + r16, columns n0 + 128 wave_n +
+  // 16 j + 4 q + e, e = 0..3; a strip is A blocks 2s, 2s + 1 (32 rows).
   const float g_a = *a_gs;
-  if constexpr (kSwiglu) {
-    // h = silu(g) u of the wave's 64 output columns c_out .. + 63 (v = acc
-    // RN32(g_a g_w) for both), staged in fp32 in the wave's strip buffer, 32
-    // rows at a time: 32 x 64 values, i.e. 128 blocks of 16, two per lane.
-    // Each lane then quantizes its blocks with the quantize kernel's
-    // arithmetic and stores 8 code bytes and 1 scale byte per block (and, if
-    // asked, the 16 fp32 values).
-    static_assert(kStripBytes >= 32 * 64 * 4, "fp32 strip of 32 x 64");
-    const float alpha = g_a * cs.gs[0];
-    const int c_out = n0 / 2 + 64 * wave_n;
-    float* fs = reinterpret_cast<float*>(smem + STAGES * kStageBytes + wave * kStripBytes);
-    const float hg = *sw.gs, r6 = __builtin_amdgcn_rcpf(6.0f * hg);
-    const int qr = lane >> 2, qb = lane & 3;  // the lane's blocks: rows qr and 16 + qr, 16-column block qb
-    if (c_out < sw.F) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        // the 32 rows of block i, every lane writing its values
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float gv = acc[2 * jj][i][v] * alpha, uv = acc[2 * jj + 1][i][v] * alpha;
-            fs[r32 * 64 + 32 * jj + (v >> 2) * 8 + half * 4 + (v & 3)] = silu_fast(gv) * uv;
-          }
-        __asm__ volatile("" ::: "memory");  // other lanes' values are read below
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          const int row = m0 + wave_m * WM + i * 32 + sub * 16 + qr;
-          const floatx4_t* src = reinterpret_cast<const floatx4_t*>(fs + (sub * 16 + qr) * 64 + 16 * qb);
-          float vals[16];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const floatx4_t f4 = src[e];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) vals[4 * e + t] = f4[t];
-          }
-          if (row < M) {
-            uint32_t w0, w1;
-            const uint32_t sc = quantize_block(vals, hg, r6, w0, w1);
-            const int col = c_out + 16 * qb;
-            *reinterpret_cast<u32x2_t*>(sw.codes + (int64_t)row * (sw.F / 2) + col / 2) = u32x2_t{w0, w1};
-            sw.scales[(int64_t)row * (sw.F / 16) + col / 16] = (uint8_t)sc;
-            if (sw.h) {
-              floatx4_t* dst = reinterpret_cast<floatx4_t*>(sw.h + (int64_t)row * sw.ldh + col);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) dst[e] = floatx4_t{vals[4 * e], vals[4 * e + 1], vals[4 * e + 2], vals[4 * e + 3]};
-            }
-          }
-        }
-        // the stores above must have read their data registers before the
-        // next block's LDS reads may land in them (as in the strip path)
-        __builtin_amdgcn_s_waitcnt(0xCF0F);  // expcnt(0); vmcnt, lgkmcnt untouched
-        __asm__ volatile("" ::: "memory");  // reads done before the next block is written
-      }
-    }
-    return;
-  }
   const int c_first = n0 + wave_n * WN, c_last = min(c_first + WN, N) - 1;
   const int s_first = col_range(cs, c_first);
   float* const alpha_tab = reinterpret_cast<float*>(smem + STAGES * kStageBytes + 4 * kStripBytes) + wave * WN;
@@ -806,133 +1088,120 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     alpha_tab[lane] = col_alpha(g_a, cs, c_first + lane);
     alpha_tab[lane + 64] = col_alpha(g_a, cs, c_first + lane + 64);
   }
-  // kGates (instantiated only for GEMMs that have gate columns): a wave
-  // whose columns meet a gate range takes its own path and leaves; every
-  // other wave takes the strip path below, the same code as without gates.
-  // (A branch on the gate inside the unrolled strip loop made every wave of
-  // a gated GEMM 18% slower.)  The gated path stages acc * alpha in fp32,
-  // 16 rows x 64 columns at a time, in the wave's strip buffer, then applies
-  // the gate functions in a rolled loop over it (one copy of their code) and
-  // stores element by element.  No workgroup barrier follows, so leaving
-  // early is safe.
+  // kGates: a wave whose columns meet a gate range stages acc * alpha in
+  // fp32, 16 rows x 64 columns at a time, in its strip buffer, applies the
+  // gate functions in a rolled loop over it and stores element by element,
+  // then leaves (no workgroup barrier follows); every other wave takes the
+  // strip path below.
   if constexpr (kGates) {
     static_assert(kStripBytes >= 16 * 64 * 4, "fp32 half strip");
     if (cols_gated(cs, c_first, c_last)) {
       float* fs = reinterpret_cast<float*>(smem + STAGES * kStageBytes + wave * kStripBytes);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FB; ++i)
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+        for (int hc = 0; hc < 2; ++hc) {
 #pragma unroll
-          for (int hc = 0; hc < 2; ++hc) {
-            if ((r32 >> 4) == sub) {
+          for (int jl = 0; jl < 4; ++jl) {
+            const int j = 4 * hc + jl, cl = 16 * j + 4 * q;  // column within the wave's 128
+            const floatx4_t al4 = *reinterpret_cast<const floatx4_t*>(alpha_tab + cl);
+            floatx4_t o;
 #pragma unroll
-              for (int j = 2 * hc; j < 2 * hc + 2; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                  const int cl = j * 32 + (v >> 2) * 8 + half * 4 + (v & 3);  // column within the wave's 128
-                  fs[(r32 & 15) * 64 + cl - 64 * hc] = acc[j][i][v] * alpha_tab[cl];
-                }
-            }
-            __asm__ volatile("" ::: "memory");  // other lanes' values are read below
-            const int row0 = m0 + wave_m * WM + i * 32 + sub * 16, col0 = c_first + 64 * hc;
-#pragma unroll 1
-            for (int e = lane; e < 16 * 64; e += 64) {
-              const int row = row0 + e / 64, col = col0 + e % 64;
-              if (row < M && col < N) {
-                const float o = col_gate(cs, col, fs[e]);
-                if constexpr (kOutBf16)
-                  reinterpret_cast<__bf16*>(y)[(int64_t)row * ldy + col] = (__bf16)o;
-                else
-                  reinterpret_cast<float*>(y)[(int64_t)row * ldy + col] = o;
-              }
-            }
-            __builtin_amdgcn_s_waitcnt(0xCF0F);  // expcnt(0): store data read before reuse
-            __asm__ volatile("" ::: "memory");  // reads done before the next pass writes
+            for (int e = 0; e < 4; ++e) o[e] = acc[j][i][e] * al4[e];
+            *reinterpret_cast<floatx4_t*>(fs + r16 * 64 + cl - 64 * hc) = o;
           }
+          __asm__ volatile("" ::: "memory");  // other lanes' values are read below
+          const int row0 = m0 + wave_m * WM + 16 * i, col0 = c_first + 64 * hc;
+#pragma unroll 1
+          for (int e = lane; e < 16 * 64; e += 64) {
+            const int row = row0 + e / 64, col = col0 + e % 64;
+            if (row < M && col < N) {
+              const float o = col_gate(cs, col, fs[e]);
+              if constexpr (kOutBf16)
+                reinterpret_cast<__bf16*>(y)[(int64_t)row * ldy + col] = (__bf16)o;
+              else
+                reinterpret_cast<float*>(y)[(int64_t)row * ldy + col] = o;
+            }
+          }
+          __builtin_amdgcn_s_waitcnt(0xCF0F);  // expcnt(0): store data read before reuse
+          __asm__ volatile("" ::: "memory");  // reads done before the next pass writes
+        }
       return;
     }
   }
-  {
-    const bool full_tile = vec_ok && m0 + BM <= M && n0 + BN <= N;
-    uint8_t* strip = smem + STAGES * kStageBytes + wave * kStripBytes;
-    constexpr int kChunksPerRow = kStripCols * kEsz / 16;
-    constexpr int kChunkElems = 16 / kEsz;
-    constexpr int kJPerPass = FN / kColPasses;
-    // the lane's 64 column scales (4 per group of 4 columns), read once
-    floatx4_t al[FN][4];
+  const bool full_tile = vec_ok && m0 + BM <= M && n0 + BN <= N;
+  uint8_t* strip = smem + STAGES * kStageBytes + wave * kStripBytes;
+  constexpr int kChunksPerRow = kStripCols * kEsz / 16;
+  constexpr int kChunkElems = 16 / kEsz;
+  constexpr int kJPerPass = FB / kColPasses;
+  floatx4_t al[FB];  // the lane's column scales
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+  for (int j = 0; j < FB; ++j) al[j] = *reinterpret_cast<const floatx4_t*>(alpha_tab + 16 * j + 4 * q);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) al[j][g] = *reinterpret_cast<const floatx4_t*>(alpha_tab + j * 32 + g * 8 + half * 4);
+  for (int s = 0; s < 4; ++s) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int jp = 0; jp < kColPasses; ++jp) {  // columns [kStripCols jp, kStripCols (jp + 1)) of the wave
 #pragma unroll
-      for (int jp = 0; jp < kColPasses; ++jp) {  // columns [kStripCols jp, kStripCols (jp + 1)) of the wave
-        uint8_t* rowp = strip + r32 * kStripRow;
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * s + ii;
+        uint8_t* rowp = strip + (16 * ii + r16) * kStripRow;
 #pragma unroll
-        for (int jl = 0; jl < kJPerPass; ++jl)
+        for (int jl = 0; jl < kJPerPass; ++jl) {
+          const int j = jp * kJPerPass + jl;
+          const int col = 16 * jl + 4 * q;  // within the strip
+          if constexpr (kOutBf16) {
+            typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
+            bf4_t o;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int j = jp * kJPerPass + jl;
-            const int col = jl * 32 + g * 8 + half * 4;  // within the strip
-            if constexpr (kOutBf16) {
-              typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
-              bf4_t o;
+            for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[j][i][e] * al[j][e]);
+            *reinterpret_cast<bf4_t*>(rowp + col * kEsz) = o;
+          } else {
+            floatx4_t o;
 #pragma unroll
-              for (int t = 0; t < 4; ++t) o[t] = (__bf16)(acc[j][i][4 * g + t] * al[j][g][t]);
-              *reinterpret_cast<bf4_t*>(rowp + col * kEsz) = o;
-            } else {
-              floatx4_t o;
-#pragma unroll
-              for (int t = 0; t < 4; ++t) o[t] = acc[j][i][4 * g + t] * al[j][g][t];
-              *reinterpret_cast<floatx4_t*>(rowp + col * kEsz) = o;
-            }
-          }
-        const int grow0 = m0 + wave_m * WM + i * 32;
-        const int gcol0 = n0 + wave_n * WN + jp * kStripCols;
-        constexpr int kQ = kStripRows * kChunksPerRow / 64;
-        u32x4_t d[kQ];
-#pragma unroll
-        for (int q = 0; q < kQ; ++q) {
-          const int id = q * 64 + lane;
-          d[q] = *reinterpret_cast<const u32x4_t*>(strip + (id / kChunksPerRow) * kStripRow + (id % kChunksPerRow) * 16);
-        }
-        if (full_tile) {
-          // the whole tile lies inside the output: unconditional 16-byte
-          // stores (a uniform branch; no per-lane bound checks)
-#pragma unroll
-          for (int q = 0; q < kQ; ++q) {
-            const int id = q * 64 + lane;
-            const int r = id / kChunksPerRow, c = id % kChunksPerRow;
-            out_t* dst = reinterpret_cast<out_t*>(y) + (int64_t)(grow0 + r) * ldy + gcol0 + c * kChunkElems;
-            __builtin_nontemporal_store(d[q], reinterpret_cast<u32x4_t*>(dst));
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < kQ; ++q) {
-            const int id = q * 64 + lane;
-            const int r = id / kChunksPerRow, c = id % kChunksPerRow;
-            const int grow = grow0 + r, gcol = gcol0 + c * kChunkElems;
-            if (grow < M) {
-              out_t* dst = reinterpret_cast<out_t*>(y) + (int64_t)grow * ldy + gcol;
-              if (vec_ok && gcol + kChunkElems <= N) {
-                __builtin_nontemporal_store(d[q], reinterpret_cast<u32x4_t*>(dst));
-              } else {
-                const out_t* e = reinterpret_cast<const out_t*>(&d[q]);
-                for (int t = 0; t < kChunkElems; ++t)
-                  if (gcol + t < N) dst[t] = e[t];
-              }
-            }
+            for (int e = 0; e < 4; ++e) o[e] = acc[j][i][e] * al[j][e];
+            *reinterpret_cast<floatx4_t*>(rowp + col * kEsz) = o;
           }
         }
-        // Wait until the stores above have read their data registers
-        // (expcnt) before the next strip's LDS reads may reuse them.  Without
-        // it, when the compiler places the store data in AGPRs, a later
-        // ds_read into the same AGPRs was seen to overwrite the data of a
-        // store still in flight (wrong rows in the output).
-        __builtin_amdgcn_s_waitcnt(0xCF0F);  // expcnt(0); vmcnt, lgkmcnt untouched
       }
+      const int grow0 = m0 + wave_m * WM + 32 * s;
+      const int gcol0 = n0 + wave_n * WN + jp * kStripCols;
+      constexpr int kQ = kStripRows * kChunksPerRow / 64;
+      u32x4_t d[kQ];
+#pragma unroll
+      for (int qq = 0; qq < kQ; ++qq) {
+        const int id = qq * 64 + lane;
+        d[qq] = *reinterpret_cast<const u32x4_t*>(strip + (id / kChunksPerRow) * kStripRow + (id % kChunksPerRow) * 16);
+      }
+      if (full_tile) {
+#pragma unroll
+        for (int qq = 0; qq < kQ; ++qq) {
+          const int id = qq * 64 + lane;
+          const int r = id / kChunksPerRow, c = id % kChunksPerRow;
+          out_t* dst = reinterpret_cast<out_t*>(y) + (int64_t)(grow0 + r) * ldy + gcol0 + c * kChunkElems;
+          __builtin_nontemporal_store(d[qq], reinterpret_cast<u32x4_t*>(dst));
+        }
+      } else {
+#pragma unroll
+        for (int qq = 0; qq < kQ; ++qq) {
+          const int id = qq * 64 + lane;
+          const int r = id / kChunksPerRow, c = id % kChunksPerRow;
+          const int grow = grow0 + r, gcol = gcol0 + c * kChunkElems;
+          if (grow < M) {
+            out_t* dst = reinterpret_cast<out_t*>(y) + (int64_t)grow * ldy + gcol;
+            if (vec_ok && gcol + kChunkElems <= N) {
+              __builtin_nontemporal_store(d[qq], reinterpret_cast<u32x4_t*>(dst));
+            } else {
+              const out_t* e = reinterpret_cast<const out_t*>(&d[qq]);
+              for (int t = 0; t < kChunkElems; ++t)
+                if (gcol + t < N) dst[t] = e[t];
+            }
+          }
+        }
+      }
+      // the stores above must have read their data registers (expcnt)
+      // before the next strip's LDS reads may reuse them
+      __builtin_amdgcn_s_waitcnt(0xCF0F);  // expcnt(0); vmcnt, lgkmcnt untouched
+      __asm__ volatile("" ::: "memory");  // the strip is read before it is written again
     }
   }
 }
@@ -942,16 +1211,16 @@ constexpr int kMaxSplits = 8;
 
 // Second kernel of a split tail: adds the K parts of each split tile in part
 // order (fixed, so the output is deterministic) and writes the sums as the
-// streaming kernel's epilogue does: y = sum * RN32(g_a g_w) of the column,
-// then fp32 or bf16 (RNE).  Block (t, q) covers tail tile t and the
-// accumulator groups 4q .. 4q + 3 of every thread of the workgroup that
-// computed it; thread `tid` takes the values that thread held.
-template <bool kOutBf16>
+// streaming epilogue does: y = sum * RN32(g_a g_w) of the column, then fp32
+// or bf16 (RNE), with the GDN gate functions on gate columns (kGates), as
+// the gated epilogue does.  The parts are row-major fp32 tiles [256 x 256]; block
+// (t, y) covers rows 16y .. 16y + 15 of tail tile t, thread tid the columns
+// 4 (tid % 64) .. + 3 of rows 16y + tid / 64 + 4r, r = 0..3.
+template <bool kOutBf16, bool kGates>
 __global__ __launch_bounds__(256) void split_tail_add_kernel(const SplitTail sp, const float* __restrict__ a_gs,
                                                              const ColScales cs, int M, int N,
                                                              void* __restrict__ y, int64_t ldy) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wave_m = wave >> 1, wave_n = wave & 1, r32 = lane & 31, half = lane >> 5;
+  const int tid = threadIdx.x, c4 = tid & 63, r0 = 16 * (int)blockIdx.y + (tid >> 6);
   const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
   const bool vec_ok = ((uintptr_t)y % 16 == 0) && (ldy % 4 == 0);
   int tm, tn;
@@ -959,30 +1228,32 @@ __global__ __launch_bounds__(256) void split_tail_add_kernel(const SplitTail sp,
   // RN32(g_a g_i) of every column range, once per block
   __shared__ float alpha_of_range[kMaxModules];
   if (tid < cs.n) alpha_of_range[tid] = *a_gs * cs.gs[tid];
-  const floatx4_t* base = reinterpret_cast<const floatx4_t*>(sp.part) + (size_t)blockIdx.x * sp.splits * (64 * 256);
-  // every load first (up to kMaxSplits parts of 4 groups in flight), then
-  // the sums in part order
+  const floatx4_t* base = reinterpret_cast<const floatx4_t*>(sp.part) + (size_t)blockIdx.x * sp.splits * (256 * 64);
+  // every load first (up to kMaxSplits parts of 4 rows in flight), then the
+  // sums in part order
   floatx4_t v[4][kMaxSplits];
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc)
+  for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
     for (int p = 0; p < kMaxSplits; ++p)
-      if (p < sp.splits) v[cc][p] = base[((size_t)p * 64 + 4 * blockIdx.y + cc) * 256 + tid];
+      if (p < sp.splits) v[rr][p] = base[(size_t)p * (256 * 64) + (r0 + 4 * rr) * 64 + c4];
   __syncthreads();  // the alpha table is written
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
-    const int c = 4 * (int)blockIdx.y + cc;
-    floatx4_t sum = v[cc][0];
+  for (int rr = 0; rr < 4; ++rr) {
+    floatx4_t sum = v[rr][0];
 #pragma unroll
     for (int p = 1; p < kMaxSplits; ++p)
-      if (p < sp.splits) sum += v[cc][p];
-    const int j = c >> 4, i = (c >> 2) & 3, g = c & 3;
-    const int row = tm * 256 + 128 * wave_m + 32 * i + r32;
-    const int col = tn * 256 + 128 * wave_n + 32 * j + 8 * g + 4 * half;
-    if (row >= M) continue;
+      if (p < sp.splits) sum += v[rr][p];
+    const int row = tm * 256 + r0 + 4 * rr;
+    const int col = tn * 256 + 4 * c4;
+    if (row >= M || col >= N) continue;
     floatx4_t o;
 #pragma unroll
     for (int t = 0; t < 4; ++t) o[t] = sum[t] * alpha_of_range[col_range(cs, min(col + t, N - 1))];
+    if constexpr (kGates) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[t] = col_gate(cs, min(col + t, N - 1), o[t]);
+    }
     if (vec_ok && col + 3 < N) {  // the 4 columns in one 8- or 16-byte store
       if constexpr (kOutBf16) {
         typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
@@ -1569,22 +1840,18 @@ hipError_t launch_stream(const uint8_t* a_codes, const uint8_t* a_scales, const 
   const int64_t tiles = ((int64_t)(M + 255) / 256) * ((N + 255) / 256);
   // whole tiles (all of them without a split), then the K parts of the tail
   // tiles, then their sums: three launches in stream order
-  gemm_stream_kernel<kStages, kOutBf16, kGates, false>
+  gemm_stream16_kernel<kStages, kOutBf16, kGates, false>
       <<<dim3((unsigned)(sp.splits > 0 ? sp.full : tiles)), dim3(256), 0, stream>>>(
-          a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y, ldy, SwigluOut{}, sp);
+          a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y, ldy, sp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || sp.splits == 0) return err;
-  if constexpr (!kGates) {
-    gemm_stream_kernel<kStages, false, false, false, true>
-        <<<dim3((unsigned)(sp.tail * sp.splits)), dim3(256), 0, stream>>>(
-            a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, nullptr, 0, SwigluOut{}, sp);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    split_tail_add_kernel<kOutBf16><<<dim3((unsigned)sp.tail, 16), dim3(256), 0, stream>>>(sp, a_gs, cs, M, N,
-                                                                                           y, ldy);
-    return hipGetLastError();
-  }
-  return hipErrorInvalidValue;  // gate epilogues are never split
+  gemm_stream16_kernel<kStages, false, false, true><<<dim3((unsigned)(sp.tail * sp.splits)), dim3(256), 0, stream>>>(
+      a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, nullptr, 0, sp);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  split_tail_add_kernel<kOutBf16, kGates><<<dim3((unsigned)sp.tail, 16), dim3(256), 0, stream>>>(sp, a_gs, cs, M, N, y,
+                                                                                                  ldy);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -1598,7 +1865,7 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   if (aligned && stream_shape(M, N, K)) {
     const bool gates = cs.decay_hi > cs.decay_lo || cs.write_hi > cs.write_lo;
     SplitTail sp{};
-    if (!gates && workspace && (uintptr_t)workspace % 16 == 0) {
+    if (workspace && (uintptr_t)workspace % 16 == 0) {
       sp = gemm_split_plan(M, N, K);
       if (workspace_bytes < gemm_split_workspace_bytes(M, N, K)) sp = SplitTail{};
       sp.part = static_cast<float*>(workspace);
@@ -1632,8 +1899,8 @@ hipError_t launch_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_
   cs.n = 1;
   cs.end[0] = (int)(2 * F);
   const int64_t tiles = ((M + 255) / 256) * ((2 * F + 255) / 256);
-  gemm_stream_kernel<3, false, false, true><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(
-      a_codes, a_scales, a_gs, w_codes, w_scales, cs, (int)M, (int)(2 * F), (int)K, nullptr, 0, out, SplitTail{});
+  gemm_swiglu_kernel<3><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, cs,
+                                                                          (int)M, (int)(2 * F), (int)K, out);
   return hipGetLastError();
 }
 

@@ -70,7 +70,7 @@ size_t gemm_split_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // The GEMM; `workspace` (16-byte aligned, workspace_bytes) lets it split the
 // last round's tiles when gemm_split_workspace_bytes() > 0 and the
-// large-tile kernel runs without gate columns; NULL / 0 runs without.
+// large-tile kernel runs; NULL / 0 runs without.
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
                        const uint8_t* w_codes, const uint8_t* w_scales, const ColScales& cs,
                        int64_t M, int64_t N, int64_t K, void* y, bool out_bf16, int64_t ldy,

@@ -30,7 +30,8 @@ def gemm_kernels_asm(tmp_path_factory):
     src = os.path.join(ROOT, "nvfp4_w4a4_quantized_05_amd", "csrc", "nvfp4_gemm.hip")
     out = tmp_path_factory.mktemp("asm") / "gemm.s"
     cmd = [hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S", "-o", str(out), src]
+           "-packed-fp32-ops", "-mllvm", "-pragma-unroll-threshold=1000000", "-I", os.path.join(ROOT, "include"),
+           "--cuda-device-only", "-S", "-o", str(out), src]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     kern, kernels = None, {}

@@ -124,8 +124,8 @@ def test_gemm_workspace_size_is_the_tail_split(lib, shape, want):
 
 def test_gemm_tail_split_needs_its_workspace(lib):
     """A shape with a tail split: too little workspace, a NULL or misaligned
-    workspace are refused before any HIP call; the gated epilogue (which never
-    splits) takes none."""
+    workspace are refused before any HIP call, by the plain, segmented and
+    gated calls alike."""
     M, N, K = 4096, 12384, 5120
     need = lib.nvfp4_gemm_workspace_size(M, N, K, 0)
     assert need > 0
@@ -136,11 +136,11 @@ def test_gemm_tail_split_needs_its_workspace(lib):
     assert lib.nvfp4_gemm(*p, M, N, K, P16, 0, N, ctypes.c_void_p(0x10008), need, None) == ALIGN
     rows = (ctypes.c_int64 * 1)(N)
     assert lib.nvfp4_gemm_segmented(*[P16] * 5, P16, rows, 1, M, K, P16, 0, N, None, 0, None) == WORKSPACE
-    # gates: no workspace needed, so the call gets past the workspace check
-    # to the gate-parameter check (a NULL a_log)
     rows3 = (ctypes.c_int64 * 3)(12288, 48, 48)
-    assert lib.nvfp4_gemm_segmented_gates(*[P16] * 5, P16, rows3, 3, 1, None, P16, 2, M, K, P16, 0, N,
-                                          None, 0, None) == NULL
+    assert lib.nvfp4_gemm_segmented_gates(*[P16] * 5, P16, rows3, 3, 1, P16, P16, 2, M, K, P16, 0, N,
+                                          None, 0, None) == WORKSPACE
+    assert lib.nvfp4_gemm_segmented_gates(*[P16] * 5, P16, rows3, 3, 1, P16, P16, 2, M, K, P16, 0, N,
+                                          None, need, None) == NULL
     assert lib.nvfp4_last_hip_error() == 0
 
 
