@@ -164,6 +164,11 @@ def measured_traffic(per_launch_bytes_alg):
     return float(t.group(1))
 
 
+def progress(msg):
+    """One line on stderr per finished phase (stdout carries only the JSON line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.clock_sampler:
@@ -232,6 +237,7 @@ def main():
              torch.empty((T, x.shape[1] // 16), dtype=torch.uint8, device=dev)) for x in xs]
     ys = [torch.empty((T, g[5]), dtype=torch.bfloat16, device=dev) for g in gemms]
     torch.cuda.synchronize()
+    progress("setup done (weights quantized, scales harmonized, inputs resident)")
 
     stream = torch.cuda.current_stream()
 
@@ -257,6 +263,7 @@ def main():
         step(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    progress(f"{args.steps} timed steps done")
 
     ms_step = wall * 1e3 / args.steps
     q_ms = {g[0]: [] for g in gemms}
@@ -367,18 +374,23 @@ def main():
     except Exception as exc:  # noqa: BLE001  (report, never fail the bench on this extra)
         amax_per_input = {"error": repr(exc)}
 
+    progress("amax pass per input done")
     extra = {} if args.no_extras else extra_measurements(nv, torch, np, dev, stream, xs, calib, qbuf, ys, in_codes,
                                                          in_scales, in_gs, in_scales_modules, module_gs,
                                                          [P[n].n for n in fused], T)
     if not args.no_extras:
+        progress("segmented-epilogue and decode measurements done")
         extra["configs"] = config_measurements(nv, torch, np, dev, stream)
+        progress("per-config measurements done")
         extra["gate_error_compression"] = gate_error_compression(nv, torch, np, dev, xs[0], calib[0], wq, w_gates,
                                                                  seed)
+        progress("gate error measurement done")
         extra["mlp_swiglu_quantize_epilogue"] = mlp_fused(nv, torch, np, dev, stream, xs, calib, qbuf, wq, gemms,
                                                           ys, T, args.steps)
         extra["gdn_recurrence_lockstep"] = gdn_lockstep(nv, torch, np, dev, xs[0], calib[0], in_codes,
                                                         in_scales_modules, module_gs, [P[n].n for n in fused],
                                                         w_fp32, seed)
+        progress("SwiGLU epilogue and recurrence measurements done")
         extra["in_proj_gates_epilogue"] = gates_epilogue_timing(nv, torch, np, dev, stream, qbuf[0], calib[0],
                                                                 in_codes, in_scales_modules, module_gs,
                                                                 [P[n].n for n in fused], ys[0], seed, T)
@@ -420,6 +432,7 @@ def main():
             roofline["frac_at_measured_clock"] = round(achieved / peak_clk, 4)
     out["step_ms_p10_p50_p90"] = pct(step_ms)
     if not args.no_cpu_baseline:
+        progress("GPU measurements done; timing the CPU oracle sample")
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows, xs, gemms, wq, fused, P, seed)
     print(json.dumps(out), flush=True)
 
