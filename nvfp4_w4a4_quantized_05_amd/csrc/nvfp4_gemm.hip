@@ -824,6 +824,13 @@ __global__ __launch_bounds__(256) void gemm_stream16_kernel(
   constexpr int kStripBytes = kStripRows * kStripRow;
   static_assert(STAGES >= 3, "ring depth");
   static_assert((STAGES - 1) * kLoadsPerStage < 64, "vmcnt range");
+  // Ring layout: the A codes of all stages, then the W codes, the A scales
+  // and the W scales, so that every LDS read below is a per-lane base
+  // register plus an immediate offset under 64 KiB.
+  constexpr int kACode = 0, kWCode = STAGES * kCodeBytes, kAScale = 2 * STAGES * kCodeBytes,
+                kWScale = kAScale + STAGES * kStageScaleBytes;
+  static_assert(kWScale + STAGES * kStageScaleBytes == STAGES * kStageBytes, "ring size");
+  static_assert((STAGES - 1) * kCodeBytes + 16 * kRowBytes * 8 < 65536, "code read offsets fit the immediate");
   constexpr int kAlphaBytes = WN * 4;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStageBytes + 4 * kStripBytes + 4 * kAlphaBytes];
   uint8_t* const ring = smem;
@@ -862,12 +869,13 @@ __global__ __launch_bounds__(256) void gemm_stream16_kernel(
     }
   };
   auto issue_one = [&](int ks, int slot, int g) {
-    uint8_t* st = ring + slot * kStageBytes;
     const uint32_t kc = (uint32_t)ks * kRowBytes, kscl = (uint32_t)ks * kScaleBytes;
-    if (g < 4) lds_copy16(ra, a_off[g], kc, st + (wave * 64 + 16 * g) * kRowBytes);
-    else if (g < 8) lds_copy16(rw, w_off[g - 4], kc, st + kCodeBytes + (wave * 64 + 16 * (g - 4)) * kRowBytes);
-    else if (g < 10) lds_copy4(ras, as_off[g - 8], kscl, st + 2 * kCodeBytes + (wave * 64 + 32 * (g - 8)) * kScaleBytes);
-    else lds_copy4(rws, ws_off[g - 10], kscl, st + 2 * kCodeBytes + kStageScaleBytes + (wave * 64 + 32 * (g - 10)) * kScaleBytes);
+    uint8_t* const codes = ring + slot * kCodeBytes;
+    uint8_t* const scales = ring + slot * kStageScaleBytes;
+    if (g < 4) lds_copy16(ra, a_off[g], kc, codes + kACode + (wave * 64 + 16 * g) * kRowBytes);
+    else if (g < 8) lds_copy16(rw, w_off[g - 4], kc, codes + kWCode + (wave * 64 + 16 * (g - 4)) * kRowBytes);
+    else if (g < 10) lds_copy4(ras, as_off[g - 8], kscl, scales + kAScale + (wave * 64 + 32 * (g - 8)) * kScaleBytes);
+    else lds_copy4(rws, ws_off[g - 10], kscl, scales + kWScale + (wave * 64 + 32 * (g - 10)) * kScaleBytes);
   };
 
   // Accumulators, zeroed in AGPRs long before the first matrix instruction
@@ -912,53 +920,77 @@ __global__ __launch_bounds__(256) void gemm_stream16_kernel(
 #pragma unroll
     for (int u = 0; u < 2; ++u) lo[p][u] = r16 * kRowBytes + 16 * (q ^ s0 ^ (2 * p)) + 8 * ((u + q) & 1);
   const uint32_t lsc = r16 * kScaleBytes + 2 * q;  // the lane's scale bytes 2q, 2q + 1 of its row
+  // The lane's LDS bases, opaque to the compiler so that it keeps them in
+  // registers instead of adding large stage offsets before every read.
+  uint32_t abase[2][2], wbase[2][2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      abase[p][u] = kACode + wave_m * WM * kRowBytes + lo[p][u];
+      wbase[p][u] = kWCode + wave_n * WN * kRowBytes + lo[p][u];
+      __asm__ volatile("" : "+v"(abase[p][u]), "+v"(wbase[p][u]));
+    }
+  uint32_t asbase = kAScale + wave_m * WM * kScaleBytes + lsc, wsbase = kWScale + wave_n * WN * kScaleBytes + lsc;
+  __asm__ volatile("" : "+v"(asbase), "+v"(wsbase));
   // v_perm selector packing the scale bytes of blocks 2k, 2k + 1 into one
   // dword, swapped for odd q so that pair u's byte is byte u (block 2k) and
   // byte 2 + u (block 2k + 1)
   const uint32_t psel = (q & 1) ? 0x04050001u : 0x05040100u;
 
   u32x2_t ra2[2][FB], rw2[2][FB];  // code pairs u = 0, 1 of the lane's rows
-  uint32_t asc[4], wsc[4], asc_n[4], wsc_n[4], xs[2 * FB];
+  uint32_t xs[2 * FB];
+  // block scales as exact fp16 values: asp[slot][b] = (scale of block b at
+  // pair 0, at pair 1) of the lane's rows in ring slot `slot` (one set per
+  // slot, so the unrolled stage loop rotates no registers)
+  half2_t asp[STAGES][FB], wsp[STAGES][FB];
   half8_t af[2][FB], wf[4];
   half2_t ta[4], tw[4];
-  uint32_t spa = 0, spw = 0;
 
-  auto read_pair = [&](uint32_t stage, int u, int g) {  // g < 8: A block g, else W block g - 8
+  auto read_pair = [&](int slot, int u, int g) {  // g < 8: A block g, else W block g - 8
     const int b = g & 7;
+    const uint32_t off = slot * kCodeBytes + 16 * kRowBytes * b;
     if (g < FB)
-      ra2[u][b] = *reinterpret_cast<const u32x2_t*>(ring + stage + wave_m * WM * kRowBytes + 16 * kRowBytes * b + lo[b & 1][u]);
+      ra2[u][b] = *reinterpret_cast<const u32x2_t*>(ring + abase[b & 1][u] + off);
     else
-      rw2[u][b] = *reinterpret_cast<const u32x2_t*>(ring + stage + kCodeBytes + wave_n * WN * kRowBytes +
-                                                    16 * kRowBytes * b + lo[b & 1][u]);
+      rw2[u][b] = *reinterpret_cast<const u32x2_t*>(ring + wbase[b & 1][u] + off);
   };
-  auto read_scale = [&](uint32_t stage, int g) {
+  auto read_scale = [&](int slot, int g) {
     const int b = g & 7;
-    const uint32_t base = g < FB ? 2 * kCodeBytes + wave_m * WM * kScaleBytes
-                                 : 2 * kCodeBytes + kStageScaleBytes + wave_n * WN * kScaleBytes;
-    xs[g] = *reinterpret_cast<const uint16_t*>(ring + stage + base + 16 * kScaleBytes * b + lsc);
+    xs[g] = *reinterpret_cast<const uint16_t*>(ring + (g < FB ? asbase : wsbase) + slot * kStageScaleBytes +
+                                               16 * kScaleBytes * b);
   };
-  auto pack_scales = [&](uint32_t (&as)[4], uint32_t (&ws)[4], int k) {  // k = 0..7
-    if (k < 4) as[k] = __builtin_amdgcn_perm(xs[2 * k + 1], xs[2 * k], psel);
-    else ws[k - 4] = __builtin_amdgcn_perm(xs[2 * (k - 4) + 9], xs[2 * (k - 4) + 8], psel);
-  };
-  // scale pair (fp16 bits) of block b at pair u
-  auto sbyte = [&](const uint32_t (&sc)[4], int b, int u) -> uint32_t {
-    return scale_pair((sc[b >> 1] >> (8 * (2 * (b & 1) + u))) & 0xFFu);
+  // k = 0..7: the scale bytes of 16-row blocks 2k', 2k' + 1 (k' = k % 4) of A
+  // (k < 4) or W packed into one dword, then converted to two fp16 pairs
+  auto pack_scales = [&](half2_t (&ap)[FB], half2_t (&wp)[FB], int k) {
+    const int kk = k & 3;
+    const uint32_t d = k < 4 ? __builtin_amdgcn_perm(xs[2 * kk + 1], xs[2 * kk], psel)
+                             : __builtin_amdgcn_perm(xs[2 * kk + 9], xs[2 * kk + 8], psel);
+    const half2_t lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, false);
+    const half2_t hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, true);
+    if (k < 4) {
+      ap[2 * kk] = lo2;
+      ap[2 * kk + 1] = hi2;
+    } else {
+      wp[2 * kk] = lo2;
+      wp[2 * kk + 1] = hi2;
+    }
   };
   auto cvt = [&](uint32_t codes, int k) -> half2_t {
-    if (k == 0) return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0);
-    if (k == 1) return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1);
-    if (k == 2) return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2);
-    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3);
+    if (k == 0) return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
+    if (k == 1) return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
+    if (k == 2) return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3);
   };
   // piece k (0..7) of dequantizing 8 codes into dst: 4 conversions, then 4
-  // multiplies by the scale pair (taken at piece 1)
-  auto piece = [&](half2_t (&tmp)[4], uint32_t& s2, uint32_t codes, uint32_t scale2, half8_t& dst, int k) {
-    if (k == 1) s2 = scale2;
+  // multiplies by half u of the block's scale pair sp (selected by the
+  // multiply's operand select, no extra instruction)
+  auto piece = [&](half2_t (&tmp)[4], uint32_t codes, half2_t sp, int u, half8_t& dst, int k) {
     if (k < 4) {
       tmp[k] = cvt(codes, k);
     } else {
-      const half2_t v = tmp[k - 4] * __builtin_bit_cast(half2_t, s2);
+      const half2_t s = u ? __builtin_shufflevector(sp, sp, 1, 1) : __builtin_shufflevector(sp, sp, 0, 0);
+      const half2_t v = tmp[k - 4] * s;
       dst[2 * (k - 4)] = v[0];
       dst[2 * (k - 4) + 1] = v[1];
     }
@@ -973,16 +1005,16 @@ __global__ __launch_bounds__(256) void gemm_stream16_kernel(
 #pragma unroll
   for (int g = 0; g < 2 * FB; ++g) read_scale(0, g);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) pack_scales(asc, wsc, k);
+  for (int k = 0; k < 8; ++k) pack_scales(asp[0], wsp[0], k);
 #pragma unroll
   for (int b = 0; b < FB; ++b)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) piece(ta, spa, ra2[0][b][0], sbyte(asc, b, 0), af[0][b], k);
+    for (int k = 0; k < 8; ++k) piece(ta, ra2[0][b][0], asp[0][b], 0, af[0][b], k);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) piece(tw, spw, rw2[0][0][0], sbyte(wsc, 0, 0), wf[0], k);
+  for (int k = 0; k < 8; ++k) piece(tw, rw2[0][0][0], wsp[0][0], 0, wf[0], k);
   // block 1: converted here, multiplied in the first slots of the loop
 #pragma unroll
-  for (int k = 0; k < 4; ++k) piece(tw, spw, rw2[0][1][0], sbyte(wsc, 1, 0), wf[1], k);
+  for (int k = 0; k < 4; ++k) piece(tw, rw2[0][1][0], wsp[0][1], 0, wf[1], k);
   // the first operands are in their registers, and 8 wait states pass,
   // before the first matrix instruction
   keep_live(af[0], wf);
@@ -993,7 +1025,6 @@ __global__ __launch_bounds__(256) void gemm_stream16_kernel(
   // so every LDS address is a loop-invariant register plus an immediate).
   auto run_stage = [&](int it, auto slot_c) {
     constexpr int slot = decltype(slot_c)::value, next_slot = (slot + 1) % STAGES;
-    constexpr uint32_t cur = (uint32_t)slot * kStageBytes, nxt = (uint32_t)next_slot * kStageBytes;
     const int refill = k_first + min(it + STAGES, k_count - 1);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -1011,9 +1042,9 @@ __global__ __launch_bounds__(256) void gemm_stream16_kernel(
         mfma16(acc[j][i], wf[j & 3], af[t & 1][i]);
         // A block j of the next step (the next stage's step 0 at t == 3)
         if (t < 3)
-          piece(ta, spa, ra2[(t + 1) >> 1][j][(t + 1) & 1], sbyte(asc, j, (t + 1) >> 1), af[(t + 1) & 1][j], i);
+          piece(ta, ra2[(t + 1) >> 1][j][(t + 1) & 1], asp[slot][j], (t + 1) >> 1, af[(t + 1) & 1][j], i);
         else
-          piece(ta, spa, ra2[0][j][0], sbyte(asc_n, j, 0), af[0][j], i);
+          piece(ta, ra2[0][j][0], asp[next_slot][j], 0, af[0][j], i);
         // W, 4 slots behind A so that no slot holds both scale extractions:
         // slots 4-7 of block j convert block j + 2, slots 0-3 multiply block
         // j + 1 (converted in block j - 1); blocks past 7 are the next
@@ -1021,17 +1052,17 @@ __global__ __launch_bounds__(256) void gemm_stream16_kernel(
         {
           const int jb = i < 4 ? j + 1 : j + 2, kw = i < 4 ? i + 4 : i - 4;
           if (jb < 8)
-            piece(tw, spw, rw2[t >> 1][jb][t & 1], sbyte(wsc, jb, t >> 1), wf[jb & 3], kw);
+            piece(tw, rw2[t >> 1][jb][t & 1], wsp[slot][jb], t >> 1, wf[jb & 3], kw);
           else if (t < 3)
-            piece(tw, spw, rw2[(t + 1) >> 1][jb - 8][(t + 1) & 1], sbyte(wsc, jb - 8, (t + 1) >> 1), wf[jb & 3], kw);
+            piece(tw, rw2[(t + 1) >> 1][jb - 8][(t + 1) & 1], wsp[slot][jb - 8], (t + 1) >> 1, wf[jb & 3], kw);
           else
-            piece(tw, spw, rw2[0][jb - 8][0], sbyte(wsc_n, jb - 8, 0), wf[jb & 3], kw);
+            piece(tw, rw2[0][jb - 8][0], wsp[next_slot][jb - 8], 0, wf[jb & 3], kw);
         }
-        if (t == 0 && n < 2 * FB) read_pair(cur, 1, n);  // pair 1 of this stage
+        if (t == 0 && n < 2 * FB) read_pair(slot, 1, n);  // pair 1 of this stage
         if (t == 2 && n < kLoadsPerStage) issue_one(refill, slot, n);
-        if (t == 2 && n >= 12 && n < 12 + 2 * FB) read_pair(nxt, 0, n - 12);  // the next stage's pair 0
-        if (t == 2 && n >= 28 && n < 28 + 2 * FB) read_scale(nxt, n - 28);    // and its scales
-        if (t == 2 && n >= 48 && (n & 1) == 0) pack_scales(asc_n, wsc_n, (n - 48) >> 1);  // not in scale slots
+        if (t == 2 && n >= 12 && n < 12 + 2 * FB) read_pair(next_slot, 0, n - 12);  // the next stage's pair 0
+        if (t == 2 && n >= 28 && n < 28 + 2 * FB) read_scale(next_slot, n - 28);    // and its scales
+        if (t == 2 && n >= 48 && (n & 1) == 0) pack_scales(asp[next_slot], wsp[next_slot], (n - 48) >> 1);
         // the operands of the matrix instruction 4 slots back stay allocated
         // until here, so no new value lands in their registers right behind
         // their last read (the previous step's at n < 4)
@@ -1043,17 +1074,24 @@ __global__ __launch_bounds__(256) void gemm_stream16_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      asc[k] = asc_n[k];
-      wsc[k] = wsc_n[k];
-    }
+    // The next stage's first operands (and W block 1's conversions) are
+    // complete here, ahead of the loop's exit test: otherwise the compiler
+    // sinks their last multiplies past the test, right in front of the
+    // matrix instructions that read them, with no wait states between.
+    keep_live(af[0], wf);
+    __asm__ volatile("" ::"v"(tw[0]), "v"(tw[1]), "v"(tw[2]), "v"(tw[3]));
+    __builtin_amdgcn_sched_barrier(0);
   };
   static_assert(STAGES == 3, "the stage loop is unrolled by the ring depth");
-  for (int it = 0; it < k_count; it += STAGES) {
+  // k_count >= 1; a pass that runs out of K steps leaves the loop at once,
+  // so the loop's back edge comes only from a full pass of STAGES steps
+  for (int it = 0;; it += STAGES) {
     run_stage(it, std::integral_constant<int, 0>{});
-    if (it + 1 < k_count) run_stage(it + 1, std::integral_constant<int, 1>{});
-    if (it + 2 < k_count) run_stage(it + 2, std::integral_constant<int, 2>{});
+    if (it + 1 >= k_count) break;
+    run_stage(it + 1, std::integral_constant<int, 1>{});
+    if (it + 2 >= k_count) break;
+    run_stage(it + 2, std::integral_constant<int, 2>{});
+    if (it + 3 >= k_count) break;
   }
   mfma16_drain();
   wait_vmcnt<0>();  // the repeated copies past the last K step
