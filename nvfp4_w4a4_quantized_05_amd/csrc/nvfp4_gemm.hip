@@ -73,6 +73,21 @@ __device__ __forceinline__ half8_t dequant8(uint32_t codes, uint32_t s2) {
   return r;
 }
 
+// 8 consecutive codes -> 8 exact fp16 values, multiplied by half `h` of the
+// fp16 scale pair sp (the multiply's operand select picks the half, so the
+// pair costs no extraction).
+__device__ __forceinline__ half8_t dequant8_sel(uint32_t codes, half2_t sp, int h) {
+  const half2_t sc = h ? __builtin_shufflevector(sp, sp, 1, 1) : __builtin_shufflevector(sp, sp, 0, 0);
+  const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * sc;
+  const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * sc;
+  const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * sc;
+  const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * sc;
+  half8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
 // Marks MFMA operands as still in use at this point of the program, so the
 // register allocator cannot hand their registers to a new value before it.
 //
@@ -1517,6 +1532,19 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     for (int j = 0; j < NB; ++j) wsd[j] = *reinterpret_cast<const uint32_t*>(wsl + (16 * j + q) * run + ts);
 #pragma unroll
     for (int b = 0; b < MB16; ++b) asd[b] = *reinterpret_cast<const uint32_t*>(asl + (16 * b + q) * run + ts);
+    // the four block scales as exact fp16 values: pair c holds the scales of
+    // chunk c (bytes 2c, 2c + 1 of the dword)
+    half2_t wsp[NB][2], asp[MB16][2];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      wsp[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wsd[j], 1.0f, false);
+      wsp[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wsd[j], 1.0f, true);
+    }
+#pragma unroll
+    for (int b = 0; b < MB16; ++b) {
+      asp[b][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(asd[b], 1.0f, false);
+      asp[b][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(asd[b], 1.0f, true);
+    }
     // operands: chunks 2g (index 0) and 2g + 1 (index 1) of the lane's row
     u32x4_t wr[NB][2], ar[MB16][2];
 #pragma unroll
@@ -1551,11 +1579,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
     // The last step's operands are kept live by the caller, past the next
     // refill.
     auto deq = [&](int s, int slot) {
-      const int c = s >> 2, dw = s & 3, sb = 8 * (2 * c + (dw >> 1));
+      const int c = s >> 2, dw = s & 3;
 #pragma unroll
-      for (int b = 0; b < MB16; ++b) av[slot][b] = dequant8(ar[b][c][dw], scale_pair((asd[b] >> sb) & 0xFFu));
+      for (int b = 0; b < MB16; ++b) av[slot][b] = dequant8_sel(ar[b][c][dw], asp[b][c], dw >> 1);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) wv[slot][j] = dequant8(wr[j][c][dw], scale_pair((wsd[j] >> sb) & 0xFFu));
+      for (int j = 0; j < NB; ++j) wv[slot][j] = dequant8_sel(wr[j][c][dw], wsp[j][c], dw >> 1);
     };
     deq(0, 0);
 #pragma unroll
