@@ -1043,6 +1043,13 @@ __global__ __launch_bounds__(256) void gemm_stream16_kernel(
     const int refill = k_first + min(it + STAGES, k_count - 1);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+      if (t == 1 || t == 3) {
+        // the LDS reads issued a step earlier (pair 1 in step 0; the next
+        // stage's scales and pair 0 in step 2) have long returned: one wait
+        // here instead of one in front of each first use
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt untouched
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (t == 2) {
         // mid-stage: the next stage has landed (own copies + barrier) and
         // every wave has read this slot (pair 1 in step 0), so the slot is
@@ -1075,8 +1082,8 @@ __global__ __launch_bounds__(256) void gemm_stream16_kernel(
         }
         if (t == 0 && n < 2 * FB) read_pair(slot, 1, n);  // pair 1 of this stage
         if (t == 2 && n < kLoadsPerStage) issue_one(refill, slot, n);
-        if (t == 2 && n >= 12 && n < 12 + 2 * FB) read_pair(next_slot, 0, n - 12);  // the next stage's pair 0
-        if (t == 2 && n >= 28 && n < 28 + 2 * FB) read_scale(next_slot, n - 28);    // and its scales
+        if (t == 2 && n >= 12 && n < 12 + 2 * FB) read_scale(next_slot, n - 12);    // the next stage's scales
+        if (t == 2 && n >= 28 && n < 28 + 2 * FB) read_pair(next_slot, 0, n - 28);  // and its pair 0
         if (t == 2 && n >= 48 && (n & 1) == 0) pack_scales(asp[next_slot], wsp[next_slot], (n - 48) >> 1);
         // the operands of the matrix instruction 4 slots back stay allocated
         // until here, so no new value lands in their registers right behind
@@ -1089,12 +1096,18 @@ __global__ __launch_bounds__(256) void gemm_stream16_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // The next stage's first operands (and W block 1's conversions) are
-    // complete here, ahead of the loop's exit test: otherwise the compiler
-    // sinks their last multiplies past the test, right in front of the
-    // matrix instructions that read them, with no wait states between.
+    // The next stage's first operands (and W block 1's conversions), its
+    // code pair 0 and its scale pairs are complete here, ahead of the loop's
+    // exit test: otherwise the compiler sinks the work that only the next
+    // stage uses past the test.  Sunk multiplies landed right in front of
+    // the matrix instructions that read them, with no wait states between;
+    // sunk LDS reads and scale conversions bunch up at the next stage's
+    // start instead of running in their slots.
     keep_live(af[0], wf);
     __asm__ volatile("" ::"v"(tw[0]), "v"(tw[1]), "v"(tw[2]), "v"(tw[3]));
+#pragma unroll
+    for (int b = 0; b < FB; ++b)
+      __asm__ volatile("" ::"v"(ra2[0][b]), "v"(rw2[0][b]), "v"(asp[next_slot][b]), "v"(wsp[next_slot][b]));
     __builtin_amdgcn_sched_barrier(0);
   };
   static_assert(STAGES == 3, "the stage loop is unrolled by the ring depth");
