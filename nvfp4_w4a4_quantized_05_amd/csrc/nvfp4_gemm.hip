@@ -14,17 +14,19 @@
 //    compute the same sum as the fp64 definition up to fp32 accumulation
 //    rounding.  fp16 and bf16 matrix throughput is the same on gfx950; fp16
 //    is used because gfx950 has a packed fp16 multiply and no packed bf16 one.
-//  * Packed codes and scale bytes are staged through LDS (4.5 bits per value,
-//    a quarter of the bytes an fp16 tile would need) and every wave
-//    dequantizes its own operand fragments in registers: per 8 values one
-//    hardware FP4->fp16 conversion per byte (with the exponent-only scale
-//    2^8) and one packed fp16 multiply per pair by the block scale taken as
-//    fp16 bits (scale byte << 7 = E4M3 value * 2^-8).  Both steps are exact.
-//  * v_mfma_f32_32x32x16_f16: a lane supplies 8 consecutive K values of one
-//    row.  Within an MFMA the K order is free as long as A and W agree, so a
-//    lane of half h reads 32 contiguous code bytes (64 K values) of its row
-//    from LDS and feeds them to 8 consecutive MFMAs; the 8 values of one MFMA
-//    always sit inside one 16-value block, i.e. one scale.
+//  * Packed codes and scale bytes are staged through LDS or registers (4.5
+//    bits per value, a quarter of the bytes an fp16 tile would need) and
+//    every wave dequantizes its own operand fragments in registers: per 8
+//    values one hardware FP4->fp16 conversion per byte and one packed fp16
+//    multiply per pair by the block scale.  The streaming and decode kernels
+//    convert two E4M3 scale bytes at a time to exact fp16 values with the
+//    hardware fp8 conversion and let the multiply's operand select pick the
+//    half; the generic kernel takes the scale as fp16 bits (scale byte << 7
+//    = E4M3 value * 2^-8, codes converted with scale 2^8).  All exact.
+//  * Within an MFMA the K order is free as long as A and W agree, and the 8
+//    values a lane supplies to one MFMA always sit inside one 16-value block,
+//    i.e. one scale.  The large shapes run on v_mfma_f32_16x16x32_f16, decode
+//    on the same instruction, the generic fallback on v_mfma_f32_32x32x16_f16.
 //  * The RN32(g_a g_w) multiply and the fp32 or bf16 (RNE) conversion happen
 //    in the epilogue, straight from the accumulators.
 #include <algorithm>
@@ -446,324 +448,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 // 16-lane phase of ds_read_b128.
 __device__ __forceinline__ int chunk_swizzle(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-// Gate/up GEMM with SwiGLU and NVFP4 quantization in its epilogue
-// (K % 128 == 0, aligned operands; the weight rows are [gate; up]).  Its
-// main loop is the earlier large-tile design on 32x32x16 matrix
-// instructions; the plain and gated GEMMs moved to gemm_stream16_kernel.
-//
-// * 256 x 256 output tile per workgroup (128 output columns: their gate and
-//   up rows), 4 waves of 128 x 128 (4 x 4 blocks of 32 x 32), accumulators
-//   in AGPRs.
-// * K tiles of 128 values stream through a STAGES-deep LDS ring filled by
-//   direct global -> LDS copies (no VGPR staging), STAGES K tiles ahead.
-// * Each K tile is consumed in two halves.  While the MFMAs of one half run,
-//   the LDS reads for the next half are in flight, and the one barrier per
-//   K tile sits between the halves: after it the slot just read can be
-//   refilled and the next K tile's first half read.  No wait on LDS or on
-//   memory is then exposed in steady state except the barrier itself.
-// * The MFMA takes W as its "A" operand and A as "B", so each lane's
-//   accumulators hold 4 consecutive output columns of one row.
-// Rows past M or F read a clamped (valid) row; their outputs are never stored.
-template <int STAGES>
-__global__ __launch_bounds__(256) void gemm_swiglu_kernel(
-    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
-    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const ColScales cs,
-    int M, int N, int K, const SwigluOut sw) {
-  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FM = 4, FN = 4;
-  constexpr int kCodeBytes = BM * kRowBytes;          // 16 KiB per operand per stage
-  constexpr int kStageScaleBytes = BM * kScaleBytes;  // 2 KiB per operand per stage
-  constexpr int kStageBytes = 2 * kCodeBytes + 2 * kStageScaleBytes;
-  constexpr int kLoadsPerStage = 12;                  // vector-memory instructions per wave per stage
-  // per-wave fp32 staging of h, 32 rows x 64 columns (rows padded by 16 bytes)
-  constexpr int kStripBytes = 32 * (64 * 4 + 16);
-  static_assert(STAGES >= 3, "ring depth");
-  static_assert((STAGES - 1) * kLoadsPerStage < 64, "vmcnt range");
-  constexpr int kAlphaBytes = WN * 4;                 // per-wave column scale table
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStageBytes + 4 * kStripBytes + 4 * kAlphaBytes];
-  uint8_t* const ring = smem;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-  const int wave_m = wave >> 1, wave_n = wave & 1;
-  const int r32 = lane & 31, half = lane >> 5;
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int64_t row_bytes = K / 2, srow_bytes = K / 16;
-  const int ksteps = K / kBK;
-
-  // Per-lane copy offsets of the current tile (32-bit, within buffer
-  // resources whose size bounds every read).  Wave w copies rows
-  // [64w, 64w+64) of both operands: codes with 4 instructions of 16 rows x 4
-  // (swizzled) 16-byte chunks, scales with 2 instructions of 32 rows x 2
-  // dwords.  Rows past the operand are clamped to its last row.
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_codes, (int64_t)M * row_bytes);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_codes, (int64_t)N * row_bytes);
-  const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_scales, (int64_t)M * srow_bytes);
-  const __amdgpu_buffer_rsrc_t rws = make_rsrc(w_scales, (int64_t)N * srow_bytes);
-  uint32_t a_off[4], w_off[4], as_off[2], ws_off[2];
-  // W row of tile row r: the tile's 256 rows are gate and up rows of its 128
-  // output columns c0 = n0 / 2 .. + 127, in blocks of 32: wave half wn =
-  // r / 128 covers columns c0 + 64 wn + 32 b + e (b = (r / 64) % 2, e = r %
-  // 32), rows 32 b .. of the half being gate (r / 32 even) or up (odd).  So
-  // a lane's accumulator blocks j = 0, 2 (gate) and 1, 3 (up) hold the same
-  // output elements.  Rows past F repeat row F - 1 (outputs past F are not
-  // written).
-  auto w_row = [&](int n0, int r) -> int {
-    const int col = n0 / 2 + 64 * (r >> 7) + 32 * ((r >> 6) & 1) + (r & 31);
-    return min(col, sw.F - 1) + (((r >> 5) & 1) ? sw.F : 0);
-  };
-  auto set_sources = [&](int m0, int n0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wave * 64 + 16 * i + (lane >> 2);
-      const int chunk = (lane & 3) ^ chunk_swizzle(row);
-      a_off[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)row_bytes + chunk * 16;
-      w_off[i] = (uint32_t)w_row(n0, row) * (uint32_t)row_bytes + chunk * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = wave * 64 + 32 * i + (lane >> 1);
-      as_off[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)srow_bytes + (lane & 1) * 4;
-      ws_off[i] = (uint32_t)w_row(n0, row) * (uint32_t)srow_bytes + (lane & 1) * 4;
-    }
-  };
-  auto issue_stage = [&](int ks, int slot) {
-    uint8_t* st = ring + slot * kStageBytes;
-    const uint32_t kc = (uint32_t)ks * kRowBytes, kscl = (uint32_t)ks * kScaleBytes;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds_copy16(ra, a_off[i], kc, st + (wave * 64 + 16 * i) * kRowBytes);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds_copy16(rw, w_off[i], kc, st + kCodeBytes + (wave * 64 + 16 * i) * kRowBytes);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      lds_copy4(ras, as_off[i], kscl, st + 2 * kCodeBytes + (wave * 64 + 32 * i) * kScaleBytes);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      lds_copy4(rws, ws_off[i], kscl, st + 2 * kCodeBytes + kStageScaleBytes + (wave * 64 + 32 * i) * kScaleBytes);
-  };
-
-  // Fragment registers: raw[.][h] holds the 16 code bytes of K-tile half h
-  // (MFMA steps 4h .. 4h+3); sc holds the 4 block scales of the K tile.
-  u32x4_t a_raw[FM][2], w_raw[FN][2];
-  uint32_t a_sc[FM], w_sc[FN], a_sc_next[FM], w_sc_next[FN];
-  auto read_half = [&](int slot, int h, bool with_scales) {
-    const uint8_t* st = ring + slot * kStageBytes;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int row = wave_m * WM + i * 32 + r32;
-      a_raw[i][h] = *reinterpret_cast<const u32x4_t*>(st + row * kRowBytes + 16 * ((2 * half + h) ^ chunk_swizzle(row)));
-      if (with_scales) a_sc_next[i] = *reinterpret_cast<const uint32_t*>(st + 2 * kCodeBytes + row * kScaleBytes + half * 4);
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int row = wave_n * WN + j * 32 + r32;
-      w_raw[j][h] = *reinterpret_cast<const u32x4_t*>(st + kCodeBytes + row * kRowBytes + 16 * ((2 * half + h) ^ chunk_swizzle(row)));
-      if (with_scales)
-        w_sc_next[j] = *reinterpret_cast<const uint32_t*>(st + 2 * kCodeBytes + kStageScaleBytes + row * kScaleBytes + half * 4);
-    }
-  };
-
-  half8_t af[2][FM], wf[2][FN];
-  auto dequant_step = [&](int kk, int slot) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-      af[slot][i] = dequant8(a_raw[i][kk >> 2][kk & 3], scale_pair((a_sc[i] >> (8 * (kk >> 1))) & 0xFFu));
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      wf[slot][j] = dequant8(w_raw[j][kk >> 2][kk & 3], scale_pair((w_sc[j] >> (8 * (kk >> 1))) & 0xFFu));
-  };
-
-
-  int tile_m, tile_n;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
-  const int m0 = tile_m * BM, n0 = tile_n * BN;
-  set_sources(m0, n0);
-  // The ring always holds STAGES copies in flight or landed.  Past the last
-  // K tile the copies repeat the last one into a slot nobody reads again,
-  // which keeps the loop body free of branches (one scheduling region, so
-  // copies and LDS reads can be interleaved with the matrix instructions).
-#pragma unroll
-  for (int s = 0; s < STAGES; ++s) issue_stage(min(s, ksteps - 1), s);
-
-  floatx16_t acc[FN][FM];  // acc[j][i]: rows of W block j (output columns) x columns of A block i (output rows)
-#pragma unroll
-  for (int j = 0; j < FN; ++j)
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
-  // Main loop: a fixed software pipeline.  Each of the 8 MFMA steps of a K
-  // tile issues its 16 MFMAs one at a time, each followed by one chunk of
-  // the dequantization of the next step (about 4-7 VALU) and, in some steps,
-  // one LDS read or one copy; a scheduling barrier after every group keeps
-  // that order, so the dequantization runs in the shadow of the matrix
-  // instructions instead of in blocks between them.  Step 7 dequantizes
-  // step 0 of the next K tile (its half 0 and scales are read at mid-tile).
-  //
-  // Operand chunks follow the order in which the previous step last read
-  // the operand's registers (W block j is last read by MFMA 4j + 3, A block
-  // i by MFMA 12 + i): W0, W1, A0, A1, A2, A3, W2, W3.
-  half2_t part[2];  // first half of an operand, between its two chunks
-  auto dequant_chunk = [&](int t, int slot, int c, bool next_tile) {
-    const int op = c >> 1, second = c & 1;
-    constexpr int kOrder[8] = {4, 5, 0, 1, 2, 3, 6, 7};  // 0..3: A blocks, 4..7: W blocks
-    const int o = kOrder[op];
-    const bool is_w = o >= 4;
-    const int idx = is_w ? o - 4 : o;
-    const uint32_t sc = is_w ? (next_tile ? w_sc_next[idx] : w_sc[idx]) : (next_tile ? a_sc_next[idx] : a_sc[idx]);
-    const uint32_t codes = is_w ? w_raw[idx][t >> 2][t & 3] : a_raw[idx][t >> 2][t & 3];
-    const half2_t sp = __builtin_bit_cast(half2_t, scale_pair((sc >> (8 * (t >> 1))) & 0xFFu));
-    if (!second) {
-      part[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * sp;
-      part[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * sp;
-    } else {
-      const half2_t q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * sp;
-      const half2_t q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * sp;
-      half8_t r;
-      r[0] = part[0][0]; r[1] = part[0][1]; r[2] = part[1][0]; r[3] = part[1][1];
-      r[4] = q0[0]; r[5] = q0[1]; r[6] = q1[0]; r[7] = q1[1];
-      if (is_w) wf[slot][idx] = r;
-      else af[slot][idx] = r;
-    }
-  };
-
-  // first K tile: wait for its copies, read its first half + scales and
-  // dequantize its step 0
-  wait_vmcnt<(STAGES - 1) * kLoadsPerStage>();
-  __builtin_amdgcn_s_barrier();
-  read_half(0, 0, true);
-#pragma unroll
-  for (int i = 0; i < FM; ++i) a_sc[i] = a_sc_next[i];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) w_sc[j] = w_sc_next[j];
-  dequant_step(0, 0);
-
-  // LDS reads of half h of a stage, one per call (g = 0..FM+FN-1 codes,
-  // then FM+FN scale dwords when with_scales)
-  auto read_one = [&](int slot, int h, int g) {
-    const uint8_t* st = ring + slot * kStageBytes;
-    if (g < FM) {
-      const int row = wave_m * WM + g * 32 + r32;
-      a_raw[g][h] = *reinterpret_cast<const u32x4_t*>(st + row * kRowBytes + 16 * ((2 * half + h) ^ chunk_swizzle(row)));
-    } else if (g < FM + FN) {
-      const int row = wave_n * WN + (g - FM) * 32 + r32;
-      w_raw[g - FM][h] = *reinterpret_cast<const u32x4_t*>(st + kCodeBytes + row * kRowBytes + 16 * ((2 * half + h) ^ chunk_swizzle(row)));
-    } else if (g < 2 * FM + FN) {
-      const int row = wave_m * WM + (g - FM - FN) * 32 + r32;
-      a_sc_next[g - FM - FN] = *reinterpret_cast<const uint32_t*>(st + 2 * kCodeBytes + row * kScaleBytes + half * 4);
-    } else {
-      const int row = wave_n * WN + (g - 2 * FM - FN) * 32 + r32;
-      w_sc_next[g - 2 * FM - FN] =
-          *reinterpret_cast<const uint32_t*>(st + 2 * kCodeBytes + kStageScaleBytes + row * kScaleBytes + half * 4);
-    }
-  };
-  // the 12 copies of one stage, one per call
-  auto issue_one = [&](int ks, int slot, int g) {
-    uint8_t* st = ring + slot * kStageBytes;
-    const uint32_t kc = (uint32_t)ks * kRowBytes, kscl = (uint32_t)ks * kScaleBytes;
-    if (g < 4) lds_copy16(ra, a_off[g], kc, st + (wave * 64 + 16 * g) * kRowBytes);
-    else if (g < 8) lds_copy16(rw, w_off[g - 4], kc, st + kCodeBytes + (wave * 64 + 16 * (g - 4)) * kRowBytes);
-    else if (g < 10) lds_copy4(ras, as_off[g - 8], kscl, st + 2 * kCodeBytes + (wave * 64 + 32 * (g - 8)) * kScaleBytes);
-    else lds_copy4(rws, ws_off[g - 10], kscl, st + 2 * kCodeBytes + kStageScaleBytes + (wave * 64 + 32 * (g - 10)) * kScaleBytes);
-  };
-
-  for (int ks = 0; ks < ksteps; ++ks) {
-    const int slot = ks % STAGES, next_slot = (ks + 1) % STAGES;
-    const int refill = min(ks + STAGES, ksteps - 1);
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int cur = kk & 1;
-      if (kk == 4) {
-        // mid-tile: K tile ks+1 has landed (own copies + barrier), and every
-        // wave is done reading this slot (its half 1 was read in step 0), so
-        // the slot is refilled with K tile ks+STAGES (clamped).  A bare
-        // s_barrier: __syncthreads() would also wait for every copy in
-        // flight and drain the ring.
-        wait_vmcnt<(STAGES - 2) * kLoadsPerStage>();
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int g = 0; g < FM * FN; ++g) {
-        const int j = g >> 2, i = g & 3;
-        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[cur][j], af[cur][i], acc[j][i], 0, 0, 0);
-        if (kk < 7) dequant_chunk(kk + 1, cur ^ 1, g, false);
-        else dequant_chunk(0, 0, g, true);  // step 0 of the next K tile
-        if (kk == 0 && g < FM + FN) read_one(slot, 1, g);  // half 1 of this K tile
-        if (kk == 4 && g < kLoadsPerStage) issue_one(refill, slot, g);
-        if (kk == 5) read_one(next_slot, 0, g);          // half 0 + scales of the next K tile
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (kk == 7) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) a_sc[i] = a_sc_next[i];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) w_sc[j] = w_sc_next[j];
-      }
-    }
-  }
-  mfma_drain();
-  wait_vmcnt<0>();  // the repeated copies past the last K tile
-  __syncthreads();  // every wave is done with the ring
-
-  const float g_a = *a_gs;
-  // h = silu(g) u of the wave's 64 output columns c_out .. + 63 (v = acc
-  // RN32(g_a g_w) for both), staged in fp32 in the wave's strip buffer, 32
-  // rows at a time: 32 x 64 values, i.e. 128 blocks of 16, two per lane.
-  // Each lane then quantizes its blocks with the quantize kernel's
-  // arithmetic and stores 8 code bytes and 1 scale byte per block (and, if
-  // asked, the 16 fp32 values).
-  static_assert(kStripBytes >= 32 * 64 * 4, "fp32 strip of 32 x 64");
-  const float alpha = g_a * cs.gs[0];
-  const int c_out = n0 / 2 + 64 * wave_n;
-  float* fs = reinterpret_cast<float*>(smem + STAGES * kStageBytes + wave * kStripBytes);
-  const float hg = *sw.gs, r6 = __builtin_amdgcn_rcpf(6.0f * hg);
-  const int qr = lane >> 2, qb = lane & 3;  // the lane's blocks: rows qr and 16 + qr, 16-column block qb
-  if (c_out < sw.F) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      // the 32 rows of block i, every lane writing its values
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float gv = acc[2 * jj][i][v] * alpha, uv = acc[2 * jj + 1][i][v] * alpha;
-          fs[r32 * 64 + 32 * jj + (v >> 2) * 8 + half * 4 + (v & 3)] = silu_fast(gv) * uv;
-        }
-      __asm__ volatile("" ::: "memory");  // other lanes' values are read below
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int row = m0 + wave_m * WM + i * 32 + sub * 16 + qr;
-        const floatx4_t* src = reinterpret_cast<const floatx4_t*>(fs + (sub * 16 + qr) * 64 + 16 * qb);
-        float vals[16];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const floatx4_t f4 = src[e];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) vals[4 * e + t] = f4[t];
-        }
-        if (row < M) {
-          uint32_t w0, w1;
-          const uint32_t sc = quantize_block(vals, hg, r6, w0, w1);
-          const int col = c_out + 16 * qb;
-          *reinterpret_cast<u32x2_t*>(sw.codes + (int64_t)row * (sw.F / 2) + col / 2) = u32x2_t{w0, w1};
-          sw.scales[(int64_t)row * (sw.F / 16) + col / 16] = (uint8_t)sc;
-          if (sw.h) {
-            floatx4_t* dst = reinterpret_cast<floatx4_t*>(sw.h + (int64_t)row * sw.ldh + col);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dst[e] = floatx4_t{vals[4 * e], vals[4 * e + 1], vals[4 * e + 2], vals[4 * e + 3]};
-          }
-        }
-      }
-      // the stores above must have read their data registers before the
-      // next block's LDS reads may land in them (a later ds_read into the
-      // registers of a store still in flight was seen to overwrite its data)
-      __builtin_amdgcn_s_waitcnt(0xCF0F);  // expcnt(0); vmcnt, lgkmcnt untouched
-      __asm__ volatile("" ::: "memory");  // reads done before the next block is written
-    }
-  }
-}
-
 // v_mfma_f32_16x16x32_f16 with the accumulator pinned in AGPRs (dst = srcC).
 // Written as inline asm because the compiler, given 64 such accumulators
 // through the builtin, shuttled them between AGPRs and VGPRs on every pass
@@ -787,7 +471,10 @@ __device__ __forceinline__ void mfma16_drain() {
 // Streaming kernel for the large shapes (K % 128 == 0, aligned operands) on
 // 16x16x32 matrix instructions: the plain epilogue (every output column
 // times its range's RN32(g_a g_w)), with kGates the GDN gate functions on
-// the gate columns, and with kSplit the K parts of a split tail.
+// the gate columns, with kSplit the K parts of a split tail, and with
+// kSwiglu the MLP's gate/up projection: h = silu(gate) up, quantized to
+// NVFP4 for the down projection in the epilogue (W = [gate; up], 128 output
+// columns per tile).
 //
 //  * 256 x 256 output tile per workgroup, 4 waves of 128 x 128 (8 x 8 blocks
 //    of 16 x 16), accumulators in AGPRs; tile order as tile_coords().
@@ -820,11 +507,11 @@ __device__ __forceinline__ void mfma16_drain() {
 //    after the register's last MFMA read.
 //  * Per stage: the next stage's pair 0 and scale bytes are read after the
 //    mid-tile barrier (step 2), pair 1 of the current stage during step 0.
-template <int STAGES, bool kOutBf16, bool kGates, bool kSplit>
+template <int STAGES, bool kOutBf16, bool kGates, bool kSplit, bool kSwiglu = false>
 __global__ __launch_bounds__(256) void gemm_stream16_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_gs,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const ColScales cs,
-    int M, int N, int K, void* __restrict__ y, int64_t ldy, const SplitTail sp) {
+    int M, int N, int K, void* __restrict__ y, int64_t ldy, const SplitTail sp, const SwigluOut sw) {
   constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FB = 8;  // 16-row blocks per operand per wave
   constexpr int kCodeBytes = BM * kRowBytes;          // 16 KiB per operand per stage
   constexpr int kStageScaleBytes = BM * kScaleBytes;  // 2 KiB per operand per stage
@@ -868,19 +555,35 @@ __global__ __launch_bounds__(256) void gemm_stream16_kernel(
   const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_scales, (int64_t)M * srow_bytes);
   const __amdgpu_buffer_rsrc_t rws = make_rsrc(w_scales, (int64_t)N * srow_bytes);
   uint32_t a_off[4], w_off[4], as_off[2], ws_off[2];
+  // W row of tile row r (0 .. 255).  Plain: row n0 + r, clamped to the last
+  // row.  kSwiglu (W = [gate (F rows); up (F rows)], N = 2F): the tile's rows
+  // are the gate and up rows of its 128 output columns c0 = n0 / 2 .. + 127,
+  // in 16-row blocks: tile row r is in wave half wn = r / 128 and that
+  // wave's W block j = (r / 16) % 8, for output column c0 + 64 wn + 16 (j / 2)
+  // + r % 16, a gate row for even j and an up row for odd j.  So a lane's
+  // accumulator blocks 2p (gate) and 2p + 1 (up) hold the same output
+  // elements.  Columns past F repeat column F - 1 (never stored).
+  auto w_row = [&](int n0, int r) -> int {
+    if constexpr (kSwiglu) {
+      const int col = n0 / 2 + 64 * (r >> 7) + 16 * ((r >> 5) & 3) + (r & 15);
+      return min(col, sw.F - 1) + (((r >> 4) & 1) ? sw.F : 0);
+    } else {
+      return min(n0 + r, N - 1);
+    }
+  };
   auto set_sources = [&](int m0, int n0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wave * 64 + 16 * i + (lane >> 2);
       const int chunk = (lane & 3) ^ chunk_swizzle(row);
       a_off[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)row_bytes + chunk * 16;
-      w_off[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)row_bytes + chunk * 16;
+      w_off[i] = (uint32_t)w_row(n0, row) * (uint32_t)row_bytes + chunk * 16;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = wave * 64 + 32 * i + (lane >> 1);
       as_off[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)srow_bytes + (lane & 1) * 4;
-      ws_off[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)srow_bytes + (lane & 1) * 4;
+      ws_off[i] = (uint32_t)w_row(n0, row) * (uint32_t)srow_bytes + (lane & 1) * 4;
     }
   };
   auto issue_one = [&](int ks, int slot, int g) {
@@ -1138,6 +841,71 @@ __global__ __launch_bounds__(256) void gemm_stream16_kernel(
     return;
   }
   __syncthreads();  // every wave is done with the ring
+
+  if constexpr (kSwiglu) {
+    // h = silu(g) u of the wave's 64 output columns c_out .. + 63 (g, u =
+    // acc RN32(g_a g_w) of W blocks 2p and 2p + 1), staged in fp32 in the
+    // wave's strip buffer 32 rows at a time (rows of 64 values padded to 68,
+    // so that the 16 rows of one write phase spread over the banks): 128
+    // blocks of 16 values, two per lane.  Each lane then quantizes its
+    // blocks with the quantize kernel's arithmetic and stores 8 code bytes
+    // and 1 scale byte per block (and, if asked, the 16 fp32 values).
+    constexpr int kHRow = 68;  // floats per staged row
+    static_assert(kStripBytes >= 32 * kHRow * 4, "fp32 strip of 32 x 64 (padded)");
+    const float alpha = *a_gs * cs.gs[0];
+    const int c_out = n0 / 2 + 64 * wave_n;
+    float* const fs = reinterpret_cast<float*>(smem + STAGES * kStageBytes + wave * kStripBytes);
+    const float hg = *sw.gs, r6 = __builtin_amdgcn_rcpf(6.0f * hg);
+    const int qr = lane >> 2, qb = lane & 3;  // the lane's blocks: rows qr and 16 + qr, 16-column block qb
+    if (c_out < sw.F) {
+#pragma unroll
+      for (int s = 0; s < FB / 2; ++s) {
+        // rows of A blocks 2s, 2s + 1: every lane writes its values
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int pp = 0; pp < FB / 2; ++pp) {
+            floatx4_t h4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              h4[e] = silu_fast(acc[2 * pp][2 * s + ii][e] * alpha) * (acc[2 * pp + 1][2 * s + ii][e] * alpha);
+            *reinterpret_cast<floatx4_t*>(fs + (16 * ii + r16) * kHRow + 16 * pp + 4 * q) = h4;
+          }
+        __asm__ volatile("" ::: "memory");  // other lanes' values are read below
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const int row = m0 + wave_m * WM + 32 * s + 16 * sub + qr;
+          const floatx4_t* src = reinterpret_cast<const floatx4_t*>(fs + (16 * sub + qr) * kHRow + 16 * qb);
+          float vals[16];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const floatx4_t f4 = src[e];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) vals[4 * e + t] = f4[t];
+          }
+          if (row < M) {
+            uint32_t w0, w1;
+            const uint32_t sc = quantize_block(vals, hg, r6, w0, w1);
+            const int col = c_out + 16 * qb;
+            *reinterpret_cast<u32x2_t*>(sw.codes + (int64_t)row * (sw.F / 2) + col / 2) = u32x2_t{w0, w1};
+            sw.scales[(int64_t)row * (sw.F / 16) + col / 16] = (uint8_t)sc;
+            if (sw.h) {
+              floatx4_t* dst = reinterpret_cast<floatx4_t*>(sw.h + (int64_t)row * sw.ldh + col);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                dst[e] = floatx4_t{vals[4 * e], vals[4 * e + 1], vals[4 * e + 2], vals[4 * e + 3]};
+            }
+          }
+        }
+        // the stores above must have read their data registers before the
+        // next pass's LDS reads may land in them (a later ds_read into the
+        // registers of a store still in flight was seen to overwrite its data)
+        __builtin_amdgcn_s_waitcnt(0xCF0F);  // expcnt(0); vmcnt, lgkmcnt untouched
+        __asm__ volatile("" ::: "memory");  // reads done before the next pass is written
+      }
+    }
+    return;
+  }
 
   // Epilogue.  Lane (r16, q) of block
   // (j, i) holds row m0 + 128 wave_m + 16 i + r16, columns n0 + 128 wave_n +
@@ -1921,11 +1689,11 @@ hipError_t launch_stream(const uint8_t* a_codes, const uint8_t* a_scales, const 
   // tiles, then their sums: three launches in stream order
   gemm_stream16_kernel<kStages, kOutBf16, kGates, false>
       <<<dim3((unsigned)(sp.splits > 0 ? sp.full : tiles)), dim3(256), 0, stream>>>(
-          a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y, ldy, sp);
+          a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, y, ldy, sp, SwigluOut{});
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || sp.splits == 0) return err;
   gemm_stream16_kernel<kStages, false, false, true><<<dim3((unsigned)(sp.tail * sp.splits)), dim3(256), 0, stream>>>(
-      a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, nullptr, 0, sp);
+      a_codes, a_scales, a_gs, w_codes, w_scales, cs, M, N, K, nullptr, 0, sp, SwigluOut{});
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   split_tail_add_kernel<kOutBf16, kGates><<<dim3((unsigned)sp.tail, 16), dim3(256), 0, stream>>>(sp, a_gs, cs, M, N, y,
@@ -1978,8 +1746,8 @@ hipError_t launch_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_
   cs.n = 1;
   cs.end[0] = (int)(2 * F);
   const int64_t tiles = ((M + 255) / 256) * ((2 * F + 255) / 256);
-  gemm_swiglu_kernel<3><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(a_codes, a_scales, a_gs, w_codes, w_scales, cs,
-                                                                          (int)M, (int)(2 * F), (int)K, out);
+  gemm_stream16_kernel<3, true, false, false, true><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(
+      a_codes, a_scales, a_gs, w_codes, w_scales, cs, (int)M, (int)(2 * F), (int)K, nullptr, 0, SplitTail{}, out);
   return hipGetLastError();
 }
 
