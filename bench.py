@@ -439,6 +439,8 @@ def main():
     if not args.no_cpu_baseline:
         progress("GPU measurements done; timing the CPU oracle sample")
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows, xs, gemms, wq, fused, P, seed)
+        progress("CPU oracle sample done; timing the CPU oracle on the small workloads")
+        out["cpu_oracle_configs"] = cpu_oracle_configs()
     print(json.dumps(out), flush=True)
 
 
@@ -1004,6 +1006,70 @@ def cpu_baseline(rows, xs, gemms, wq, fused, P, seed):
             "sample": f"first {rows} of {TOKENS} tokens of each input and 1/{frac} of each projection's "
                       f"output features: {flops / 1e9:.1f} GFLOP + {sum(s[0].size for s in samples) / 1e6:.1f}M "
                       f"values quantized in {dt:.1f} s (fp64 numpy oracle, quantize + GEMM + |a*w| sums)"}
+
+
+def cpu_oracle_configs():
+    """The CPU oracle (oracle/nvfp4_ref.py, untuned) on the small workloads in
+    full, on this host, beside the GPU's figures in `configs`: tiny (quantize
+    X in amax mode + GEMM), decode (quantize X with its tensor scale + GEMM
+    against the N = 12288 weight, each M) and the fused GDN in-projection at
+    4,096 tokens (quantize X, harmonize the four modules' scales, GEMM).  The
+    same seeded inputs as the GPU lines; weights are quantized by the oracle
+    beforehand (offline work, untimed).  Each GEMM includes the oracle's
+    sum of |a w| (its error allowance)."""
+    import numpy as np
+
+    from oracle import nvfp4_ref as ref
+    from workloads import CONFIGS, activations, normal_weights
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    out = {}
+    cfg = CONFIGS["tiny"]
+    kind, rows, cols, dtype = cfg["x"]
+    p = cfg["projections"][0]
+    x = activations(kind, rows, cols, seed=cfg["seed"], device="cpu", dtype=dtype).float().numpy()
+    w = ref.quantize(normal_weights(p.n, p.k, p.std, seed=cfg["seed"] * 100, device="cpu").numpy())
+    dt = timed(lambda: ref.gemm_ref(*ref.quantize(x), *w))
+    out["tiny"] = {"quantize_plus_gemm_ms": round(dt * 1e3, 3), "shape": f"X[{rows}x{cols}] (amax) x W[{p.n}x{p.k}]"}
+
+    cfg = CONFIGS["decode"]
+    p = cfg["projections"][0]
+    w = ref.quantize(normal_weights(p.n, p.k, p.std, seed=cfg["seed"] * 100, device="cpu").numpy())
+    per_m = {}
+    for m in cfg["ms"]:
+        xm = activations(cfg["x"][0], m, p.k, seed=cfg["seed"], device="cpu").float().numpy()
+        g = ref.global_scale(xm)
+        dt = timed(lambda xm=xm, g=g: ref.gemm_ref(*ref.quantize(xm, g=g), *w))
+        per_m[str(m)] = {"quantize_plus_gemm_ms": round(dt * 1e3, 2)}
+    out["decode"] = {"shape": f"M x {p.n} x {p.k}", "per_m": per_m}
+
+    cfg = CONFIGS["fused_gdn"]
+    T4, k4 = cfg["rows"], cfg["x"][2]
+    x4 = activations(cfg["x"][0], T4, k4, seed=cfg["seed"], device="cpu").float().numpy()
+    mods = [ref.quantize(normal_weights(q.n, q.k, q.std, seed=cfg["seed"] * 100 + i, device="cpu").numpy())
+            for i, q in enumerate(cfg["projections"])]
+    wc = np.concatenate([m[0] for m in mods])
+
+    def fused_gdn():
+        a4 = ref.quantize(x4)
+        hs, hg, _, _ = ref.harmonize_ref([m[1] for m in mods], [m[2] for m in mods])
+        ref.gemm_ref(*a4, wc, hs, hg)
+
+    dt = timed(fused_gdn)
+    fl = 2.0 * T4 * wc.shape[0] * k4
+    out["fused_gdn"] = {"quantize_harmonize_gemm_s": round(dt, 2), "gemm_tflops": round(fl / dt / 1e12, 4),
+                        "shape": f"{T4} x {wc.shape[0]} x {k4}"}
+    try:
+        from threadpoolctl import threadpool_info
+        out["blas_threads"] = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        out["blas_threads"] = None
+    out["kind"] = "oracle"
+    return out
 
 
 if __name__ == "__main__":
